@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of one HSA denoise iteration on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--loop]
+
+A step is one pass of the whole path over the single-step workload (N = 32760
+tokens on a 21x30x52 latent grid, 12 heads x 128, 64 latent channels, half of
+the tokens active): token selection by L1 relative velocity change, the active
+set, the gather of the active rows, the KV-cache scatter, active-query
+attention against all N cached rows, and the cached Euler update.  Inputs are
+seeded synthetic data already resident in HBM.  Prints one JSON line.
+
+value = attention FLOPs of the iteration (4 * |A| * N * H * D) / wall time of the
+whole iteration, in TFLOP/s; ms_per_step is that wall time.  The roofline entry
+is the attention kernel alone, timed with HIP events around each launch.
+With --loop the full 40-iteration, 30-layer schedule (T=40, budgets {40,20,10,5},
+m=4) is also run once and its mean ms per iteration reported.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_single_step_pmc.txt")
+ATTN_SRC = os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", "attn.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline sample")
+    p.add_argument("--loop", action="store_true", help="also time the full 40-iteration schedule")
+    return p.parse_args()
+
+
+def attn_source_hash() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, or None when
+    the summary is missing or was taken on a different version of the kernel source."""
+    if not os.path.exists(ATTN_PMC_SUMMARY):
+        return None
+    text = open(ATTN_PMC_SUMMARY).read()
+    h = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != attn_source_hash():
+        return None
+    return float(t.group(1))
+
+
+class SingleStep:
+    """Device state of the single-step workload and one call per path step."""
+
+    def __init__(self, hs, synth, torch):
+        self.hs, self.torch = hs, torch
+        cfg = synth.single_step()
+        self.cfg = cfg
+        N, C, H, D = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim
+        dev = torch.device("cuda")
+        vm = synth.VelocityModel(cfg)
+        src = synth.QKVSource(cfg)
+        na = hs.hsastep_n_active(N, cfg.budgets, cfg.sizes, cfg.T, cfg.m, cfg.iteration)
+        self.na = na
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        bits = lambda a: up(np.ascontiguousarray(a).view(np.int16))
+        self.v_prev, self.v_cur = up(vm.v_prev), up(vm(0))
+        self.v_model = up(vm(cfg.iteration))           # the model's velocity at this iteration
+        self.x = up(synth.latent0(cfg))
+        self.v_hat = self.v_prev.clone()
+        pre = src.prefill(0)
+        self.k_cache, self.v_cache = bits(pre), bits(pre)
+        self.q = bits(src.rows("q", 0, cfg.iteration, na))
+        self.k_new = bits(src.rows("k", 0, cfg.iteration, na))
+        self.v_new = bits(src.rows("v", 0, cfg.iteration, na))
+        self.out = torch.empty_like(self.q)
+        self.group_id = torch.empty(N, dtype=torch.int32, device=dev)
+        self.active_idx = torch.empty(N, dtype=torch.int32, device=dev)
+        self.active_pos = torch.empty(N, dtype=torch.int32, device=dev)
+        self.x_act = torch.empty((na, C), dtype=torch.float32, device=dev)
+        self.v_fresh = torch.empty((na, C), dtype=torch.float32, device=dev)
+        self.ws = hs.workspace(N, cfg.n_groups, dev)
+        sig = np.linspace(1.0, 0.0, cfg.T + 1, dtype=np.float64).astype(np.float32)
+        self.s_cur, self.s_next = float(sig[cfg.iteration]), float(sig[cfg.iteration + 1])
+        self.scale = float(np.float32(1.0 / np.sqrt(D)))
+        self.flops = 4.0 * cfg.batch * na * N * H * D
+
+    def step(self, ev=None):
+        hs, c = self.hs, self.cfg
+        hs.hsa_select_groups(self.v_prev, self.v_cur, c.sizes, self.group_id, None, self.ws)
+        na = hs.hsa_active_set(self.group_id, c.budgets, c.sizes, c.T, c.m, c.iteration,
+                               self.active_idx, self.active_pos, self.ws)
+        hs.hsastep_gather_rows(self.x_act, self.x, self.active_idx, na)      # model input rows
+        hs.hsastep_gather_rows(self.v_fresh, self.v_model, self.active_idx, na)  # model stand-in
+        hs.hsa_kv_update(self.k_cache, self.v_cache, self.k_new, self.v_new, self.active_idx, na)
+        if ev is not None:
+            ev[0].record()
+        hs.hsa_attention_active(self.q, self.k_cache, self.v_cache, self.out, self.scale)
+        if ev is not None:
+            ev[1].record()
+        hs.hsa_euler_step(self.x, self.v_hat, self.v_fresh, self.active_pos, na, self.s_cur,
+                          self.s_next)
+
+
+def cpu_baseline(budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload: the full selection,
+    active set, KV scatter and Euler update, plus attention for a sample of active query rows
+    (all heads), extrapolated linearly to all |A| rows (every row costs the same)."""
+    import oracle
+    from sparse_attention_l1_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cfg = synth.single_step()
+    vm = synth.VelocityModel(cfg)
+    src = synth.QKVSource(cfg)
+    i = cfg.iteration
+    vp, vc = vm.v_prev, vm(0)
+    x0 = synth.latent0(cfg)
+    v_model = vm(i)
+    t0 = time.perf_counter()
+    g, _ = oracle.select_groups(vp, vc, cfg.sizes)
+    idx, pos = oracle.active_set(g, cfg.budgets, cfg.T, cfg.m, i)
+    na = idx.shape[0]
+    xa = x0[idx]
+    pre = src.prefill(0)
+    kc, vcache = pre.copy(), pre.copy()
+    kn, vn, q = (src.rows(t, 0, i, na) for t in ("k", "v", "q"))
+    oracle.kv_update(kc, vcache, kn, vn, idx)
+    oracle.euler_step(x0, vp, v_model[idx], idx, np.float32(0.875), np.float32(0.85))
+    t_rest = time.perf_counter() - t0
+    scale = float(np.float32(1.0 / np.sqrt(cfg.head_dim)))
+    rows = 32
+    t1 = time.perf_counter()
+    oracle.attention_active(q[:, :rows], kc, vcache, scale)
+    t_first = time.perf_counter() - t1
+    # grow the sample to fill the budget
+    per_row = t_first / rows
+    more = int(max(0, min(na - rows, (budget_s - t_rest - t_first) / max(per_row, 1e-9))))
+    t_more = 0.0
+    if more > 0:
+        sel = synth.sample_rows(cfg.cfg_id, na, more, tag=1)
+        t2 = time.perf_counter()
+        oracle.attention_active(q[:, sel], kc, vcache, scale)
+        t_more = time.perf_counter() - t2
+    sampled = rows + more
+    t_attn = (t_first + t_more) * na / sampled
+    t_step = t_rest + t_attn
+    flops = 4.0 * na * cfg.n_tokens * cfg.heads * cfg.head_dim
+    del xa
+    return {"value": flops / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"single step N=32760: selection, active set, KV scatter and Euler in full; "
+                       f"attention for {sampled} of {na} active query rows x 12 heads, "
+                       f"extrapolated linearly; {t_rest + t_first + t_more:.1f} s of CPU time, "
+                       f"extrapolated step {t_step:.1f} s")}
+
+
+def run_loop(hs, synth, torch):
+    """Full 40-iteration schedule, 30 layers (T=40, budgets {40,20,10,5}, m=4): mean ms per
+    iteration of the whole path with the synthetic model stand-in (pool windows on device)."""
+    from sparse_attention_l1_amd.sampler import HsaSampler
+    cfg = synth.full_schedule()
+    dev = torch.device("cuda")
+    N, C, H, D = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim
+    src = synth.QKVSource(cfg)
+    vm = synth.VelocityModel(cfg)
+    pools = {t: torch.from_numpy(src.pools[t].bits.view(np.int16)).to(dev) for t in "qkv"}
+    pre = torch.from_numpy(src.prefill(0).view(np.int16)).to(dev)
+    v_all = [torch.from_numpy(vm(i)).to(dev) for i in range(cfg.T)]
+
+    class PoolModel:
+        def qkv(self, l, i, active_idx, na):
+            need = na * H * D
+            return tuple(pools[t][src.pools[t].offset(need, 0, l, i):][:need].view(1, na, H, D)
+                         for t in "qkv")
+
+        def velocity(self, i, active_idx, na):
+            out = vbuf[:na]
+            hs.hsastep_gather_rows(out, v_all[i], active_idx, na)
+            return out
+
+    vbuf = torch.empty((N, C), dtype=torch.float32, device=dev)
+    smp = HsaSampler(n_tokens=N, channels=C, batch=1, heads=H, head_dim=D, layers=cfg.layers,
+                     T=cfg.T, budgets=cfg.budgets, group_sizes=cfg.sizes, m=cfg.m)
+    smp.reset(torch.from_numpy(synth.latent0(cfg)).to(dev), torch.from_numpy(vm.v_prev).to(dev),
+              lambda l: (pre, pre))
+    model = PoolModel()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(cfg.T)]
+    flops = 0.0
+    t0 = time.perf_counter()
+    for i in range(cfg.T):
+        evs[i][0].record()
+        smp.iteration(i, model)
+        evs[i][1].record()
+        flops += 4.0 * smp.n_active * N * H * D * cfg.layers
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_iter = [a.elapsed_time(b) for a, b in evs]
+    return {"workload": cfg.name, "iterations": cfg.T, "layers": cfg.layers,
+            "ms_per_iteration_mean": float(np.mean(per_iter)),
+            "ms_per_iteration": [round(x, 3) for x in per_iter],
+            "attention_pflop": flops / 1e15, "tflops_effective": flops / wall / 1e12,
+            "wall_s": wall}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the HSA path is built and "
+              f"timed on a single MI355X; multi-GPU sharding is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_attention_l1_amd import hsastep as hs
+    from sparse_attention_l1_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    print("bench: building single-step inputs", file=sys.stderr, flush=True)
+    st = SingleStep(hs, synth, torch)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    print("bench: timing", file=sys.stderr, flush=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        st.step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    achieved = st.flops / (attn_ms * 1e-3) / 1e12
+    traffic = load_traffic()
+    res = {
+        "metric": "HSA active-query attention TFLOP/s + ms per denoise iteration at N=32760",
+        "value": st.flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V and cache, lognormal-drift fp32 velocities)",
+        "config": {"workload": st.cfg.name, "n_tokens": st.cfg.n_tokens, "n_active": st.na,
+                   "heads": st.cfg.heads, "head_dim": st.cfg.head_dim,
+                   "channels": st.cfg.channels, "batch": st.cfg.batch,
+                   "groups": {"budgets": list(st.cfg.budgets), "sizes": list(st.cfg.sizes),
+                              "T": st.cfg.T, "m": st.cfg.m, "iteration": st.cfg.iteration}},
+        "attention_ms_per_launch": attn_ms,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic},
+    }
+    if args.loop:
+        print("bench: full schedule loop", file=sys.stderr, flush=True)
+        res["full_schedule"] = run_loop(hs, synth, torch)
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,43 @@
+// Internal launchers of the HSA kernels (one per .hip file).  Each validates
+// nothing: the C ABI layer (abi.cpp) checks arguments before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace hsastep {
+
+// score.hip: r[n] = L1 relative change of token n (balanced-tree fp32 sums).
+hipError_t launch_score(const float* v_prev, const float* v_cur, int64_t n_tokens, int channels,
+                        float* r, hipStream_t stream);
+
+// rank.hip: group id from the rank of r (largest first, ties by index).
+// targets[t] = first rank of group t+1 (only targets < n_tokens are passed).
+hipError_t launch_rank(const float* r, int64_t n_tokens, const int64_t* targets, int n_targets,
+                       int32_t* group_id, hipStream_t stream);
+
+// active.hip: ascending active index list + inverse map for one iteration.
+hipError_t launch_active(const int32_t* group_id, int64_t n_tokens, uint32_t group_mask,
+                         int n_groups, int32_t* active_idx, int32_t* active_pos, int32_t* blockcnt,
+                         hipStream_t stream);
+
+// rows.hip: row gather and the KV-cache row scatter.
+hipError_t launch_gather(void* dst, const void* src, const int32_t* index, int64_t n_rows,
+                         int64_t n_src_rows, int64_t row_bytes, hipStream_t stream);
+hipError_t launch_kv_update(uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_new,
+                            const uint16_t* v_new, const int32_t* active_idx, int64_t n_active,
+                            int64_t n_tokens, int batch, int heads, int head_dim,
+                            hipStream_t stream);
+
+// attn.hip: active-query full-context attention (bf16 MFMA, fp32 online softmax).
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                            uint16_t* out, int64_t n_active, int64_t n_tokens, int batch, int heads,
+                            int head_dim, float softmax_scale, hipStream_t stream);
+
+// euler.hip: cached Euler update over all tokens.
+hipError_t launch_euler(float* x, float* v_cache, const float* v_fresh, const int32_t* active_pos,
+                        int64_t n_active, int64_t n_tokens, int channels, float sigma_cur,
+                        float sigma_next, hipStream_t stream);
+
+}  // namespace hsastep
