@@ -23,6 +23,8 @@ SOURCES = ["abi.cpp", "host.cpp", "score.hip", "rank.hip", "active.hip", "rows.h
            "attn.hip"]
 
 ARCH = "gfx950"
+# files whose fp32 results are specified to the bit: no multiply-add contraction
+EXACT = ("score.hip", "euler.hip")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 # device code: gfx950 only; no packed-fp32 instructions (v_pk_{add,mul,fma}_f32)
@@ -41,6 +43,8 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
     if src.endswith(".hip"):
         cmd += ["-x", "hip"] + DEVICE
+    if src in EXACT:
+        cmd += ["-ffp-contract=off"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -222,10 +222,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[s][j]);
-    if (__ballot(mx * c_log2 > m_run + kTau)) {
+    const bool need = mx * c_log2 > m_run + kTau;
+    if (__ballot(need)) {
+      // the decision is per query (lanes l and l^32), never per wavefront, so a
+      // query's result does not depend on which other queries share its tile
       const float mo = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mo * c_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const int other_need = __shfl_xor(int(need), 32);   // every lane takes part
+      const bool pair_need = need || other_need != 0;
+      const float m_new = pair_need ? fmaxf(m_run, mo * c_log2) : m_run;
+      const float alpha = pair_need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int e = 0; e < NE; ++e)

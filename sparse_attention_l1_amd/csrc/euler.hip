@@ -35,10 +35,11 @@ __global__ __launch_bounds__(256) void euler_vec4_kernel(float4* __restrict__ x,
     const float4 v = *src;
     float4 xv = x[t];
     if (act) v_cache[t] = v;
-    xv.x = __fadd_rn(xv.x, __fmul_rn(dt, v.x));
-    xv.y = __fadd_rn(xv.y, __fmul_rn(dt, v.y));
-    xv.z = __fadd_rn(xv.z, __fmul_rn(dt, v.z));
-    xv.w = __fadd_rn(xv.w, __fmul_rn(dt, v.w));
+    // contraction is off in this scope (and for the file): product, then sum
+    xv.x = xv.x + dt * v.x;
+    xv.y = xv.y + dt * v.y;
+    xv.z = xv.z + dt * v.z;
+    xv.w = xv.w + dt * v.w;
     x[t] = xv;
   }
 }
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void euler_scalar_kernel(float* __restrict__ x
     const float* src = act ? v_fresh + int64_t(pos) * channels + c : v_cache + t;
     const float v = *src;
     if (act) v_cache[t] = v;
-    x[t] = __fadd_rn(x[t], __fmul_rn(dt, v));
+    x[t] = x[t] + dt * v;   // no contraction: see the pragma
   }
 }
 

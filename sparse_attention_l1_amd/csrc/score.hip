@@ -55,22 +55,22 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ v_
   float d[4], a[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    d[j] = fabsf(__fsub_rn(c[j], p[j]));
+    d[j] = fabsf(c[j] - p[j]);
     a[j] = fabsf(p[j]);
   }
-  float num = __fadd_rn(__fadd_rn(d[0], d[1]), __fadd_rn(d[2], d[3]));
-  float den = __fadd_rn(__fadd_rn(a[0], a[1]), __fadd_rn(a[2], a[3]));
+  float num = (d[0] + d[1]) + (d[2] + d[3]);
+  float den = (a[0] + a[1]) + (a[2] + a[3]);
 #pragma unroll
   for (int off = 1; off < P; off <<= 1) {
-    num = __fadd_rn(num, __shfl_xor(num, off));
-    den = __fadd_rn(den, __shfl_xor(den, off));
+    num = num + __shfl_xor(num, off);
+    den = den + __shfl_xor(den, off);
   }
   if (lane == 0) {
     float q;
     if (den == 0.0f)
       q = (num == 0.0f) ? 0.0f : INFINITY;
     else
-      q = __fdiv_rn(num, den);
+      q = num / den;   // IEEE round-to-nearest (correctly rounded divide is on)
     if (q != q) q = INFINITY;   // NaN -> +inf
     r[token] = q;
   }

@@ -23,13 +23,17 @@ def hs():
     return hsastep
 
 
-def attn_close(got_bits, want, label):
+def attn_close(got_bits, want, label, absolute=True):
+    """absolute: the 2e-2 max-abs bar (unit-variance inputs, |O| well below 1).  For peaky
+    softmaxes |O| reaches the range where one bf16 output ulp alone is 2^-7 * |O| (0.0156 at
+    |O| = 4), so only the resolution-relative bound 2^-7 * max|O| + 2e-3 applies there."""
     got = bf16_to_f64(got_bits)
     err = np.abs(got - want)
     mx = float(np.max(np.abs(want))) if want.size else 0.0
     worst = float(err.max()) if err.size else 0.0
     print(f"[{label}] attention max-abs err {worst:.3e}, max|O| {mx:.3e}", flush=True)
-    assert worst <= ATOL
+    if absolute:
+        assert worst <= ATOL
     assert worst <= 2.0 ** -7 * mx + 2e-3
 
 
@@ -174,7 +178,7 @@ def test_attention(hs, B, A, N, H, D, qs):
     o = out[: B * A * H * D].view(B, A, H, D)
     hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
     torch.cuda.synchronize()
-    attn_close(host_bits(o), want, f"B{B} A{A} N{N} H{H} D{D} x{qs}")
+    attn_close(host_bits(o), want, f"B{B} A{A} N{N} H{H} D{D} x{qs}", absolute=qs == 1.0)
     assert bool((out[B * A * H * D:] == 0x7F7F).all())
     # determinism, and independence of a query from its tile neighbours
     o2 = torch.empty_like(o)
