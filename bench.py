@@ -44,7 +44,22 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--loop", action="store_true", help="also time the full 40-iteration schedule")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 512 MiB device copy 3 times (reference for HBM counters)")
     return p.parse_args()
+
+
+def copy_calibration(torch):
+    """A plain copy of known size: 512 MiB read + 512 MiB written per launch.  Under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives the counters' scale on this GPU."""
+    n = 512 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
+                      "launches": 3}))
 
 
 def attn_source_hash() -> str:
@@ -236,6 +251,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     print("bench: building single-step inputs", file=sys.stderr, flush=True)
     st = SingleStep(hs, synth, torch)
     torch.cuda.synchronize()
