@@ -41,9 +41,12 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--loop", action="store_true", help="also time the full 40-iteration schedule")
+    p.add_argument("--sweep", action="store_true",
+                   help="also time the large-head sweep: N=75600, 40x128 heads, active fraction "
+                        "1, 1/2, 1/4, 1/8 (attention, selection, scatter, Euler per kernel)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy 3 times (reference for HBM counters)")
     return p.parse_args()
@@ -154,7 +157,7 @@ def cpu_baseline(budget_s: float):
     g, _ = oracle.select_groups(vp, vc, cfg.sizes)
     idx, pos = oracle.active_set(g, cfg.budgets, cfg.T, cfg.m, i)
     na = idx.shape[0]
-    xa = x0[idx]
+    x0[idx]                      # gather of the active rows (model input)
     pre = src.prefill(0)
     kc, vcache = pre.copy(), pre.copy()
     kn, vn, q = (src.rows(t, 0, i, na) for t in ("k", "v", "q"))
@@ -162,29 +165,24 @@ def cpu_baseline(budget_s: float):
     oracle.euler_step(x0, vp, v_model[idx], idx, np.float32(0.875), np.float32(0.85))
     t_rest = time.perf_counter() - t0
     scale = float(np.float32(1.0 / np.sqrt(cfg.head_dim)))
-    rows = 32
-    t1 = time.perf_counter()
-    oracle.attention_active(q[:, :rows], kc, vcache, scale)
-    t_first = time.perf_counter() - t1
-    # grow the sample to fill the budget
-    per_row = t_first / rows
-    more = int(max(0, min(na - rows, (budget_s - t_rest - t_first) / max(per_row, 1e-9))))
-    t_more = 0.0
-    if more > 0:
-        sel = synth.sample_rows(cfg.cfg_id, na, more, tag=1)
+    # attention on seeded samples of active query rows, grown until the CPU budget is used
+    order = synth.sample_rows(cfg.cfg_id, na, na, tag=1)
+    rows, t_attn_s, chunk = 0, 0.0, 64
+    while rows < na and t_rest + t_attn_s < budget_s:
+        sel = np.sort(order[rows:rows + chunk])
         t2 = time.perf_counter()
         oracle.attention_active(q[:, sel], kc, vcache, scale)
-        t_more = time.perf_counter() - t2
-    sampled = rows + more
-    t_attn = (t_first + t_more) * na / sampled
+        t_attn_s += time.perf_counter() - t2
+        rows += sel.size
+        chunk = min(chunk * 2, 2048)
+    t_attn = t_attn_s * na / rows
     t_step = t_rest + t_attn
     flops = 4.0 * na * cfg.n_tokens * cfg.heads * cfg.head_dim
-    del xa
     return {"value": flops / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"single step N=32760: selection, active set, KV scatter and Euler in full; "
-                       f"attention for {sampled} of {na} active query rows x 12 heads, "
-                       f"extrapolated linearly; {t_rest + t_first + t_more:.1f} s of CPU time, "
+                       f"attention for {rows} of {na} active query rows x 12 heads, "
+                       f"extrapolated linearly; {t_rest + t_attn_s:.1f} s of CPU time, "
                        f"extrapolated step {t_step:.1f} s")}
 
 
@@ -236,6 +234,70 @@ def run_loop(hs, synth, torch):
             "ms_per_iteration": [round(x, 3) for x in per_iter],
             "attention_pflop": flops / 1e15, "tflops_effective": flops / wall / 1e12,
             "wall_s": wall}
+
+
+def run_sweep(hs, synth, torch, reps=5):
+    """Large-head sweep (N=75600 on a 21x45x80 grid, 40 heads x 128, 64 channels): per active
+    fraction f, each kernel of one iteration timed alone with HIP events (mean of reps).
+    Q/K/V and the cache are seeded N(0,1) values drawn on the device."""
+    dev = torch.device("cuda")
+    out = {"workload": "large-head sweep N=75600 21x45x80, 40x128, 1 layer", "points": []}
+    gen = torch.Generator(device=dev).manual_seed(20260512)
+    N, H, D = 75600, 40, 128
+    kc = torch.randn((1, N, H, D), device=dev, generator=gen).to(torch.bfloat16)
+    vc = torch.randn((1, N, H, D), device=dev, generator=gen).to(torch.bfloat16)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for f in (1.0, 0.5, 0.25, 0.125):
+        cfg = synth.sweep(f)
+        C = cfg.channels
+        vm = synth.VelocityModel(cfg)
+        vp = torch.from_numpy(vm.v_prev).to(dev)
+        vcur = torch.from_numpy(vm(0)).to(dev)
+        g = torch.empty(N, dtype=torch.int32, device=dev)
+        idx = torch.empty(N, dtype=torch.int32, device=dev)
+        pos = torch.empty(N, dtype=torch.int32, device=dev)
+        ws = hs.workspace(N, cfg.n_groups, dev)
+        hs.hsa_select_groups(vp, vcur, cfg.sizes, g, None, ws)
+        na = hs.hsa_active_set(g, cfg.budgets, cfg.sizes, cfg.T, cfg.m, cfg.iteration, idx, pos, ws)
+        q = torch.randn((1, na, H, D), device=dev, generator=gen).to(torch.bfloat16)
+        kn = torch.randn((1, na, H, D), device=dev, generator=gen).to(torch.bfloat16)
+        vn = torch.randn((1, na, H, D), device=dev, generator=gen).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        x = torch.from_numpy(synth.latent0(cfg)).to(dev)
+        vh = vp.clone()
+        vf = torch.empty((na, C), dtype=torch.float32, device=dev)
+        hs.hsastep_gather_rows(vf, vcur, idx, na)
+        flops = 4.0 * na * N * H * D
+        t_att = timed(lambda: hs.hsa_attention_active(q, kc, vc, o, scale))
+        t_sel = timed(lambda: hs.hsa_select_groups(vp, vcur, cfg.sizes, g, None, ws))
+        t_act = timed(lambda: hs.hsa_active_set(g, cfg.budgets, cfg.sizes, cfg.T, cfg.m,
+                                                cfg.iteration, idx, pos, ws))
+        t_kv = timed(lambda: hs.hsa_kv_update(kc, vc, kn, vn, idx, na))
+        t_eu = timed(lambda: hs.hsa_euler_step(x, vh, vf, pos, na, 0.875, 0.85))
+        kv_bytes = 4.0 * na * H * D * 2 + 4 * na
+        eu_bytes = 3.0 * N * C * 4 + na * C * 4 + 4 * N
+        out["points"].append({
+            "active_fraction": f, "n_active": na,
+            "attention_ms": t_att, "attention_tflops": flops / t_att / 1e9,
+            "attention_frac_of_bf16_peak": flops / t_att / 1e9 / PEAK_BF16_TFLOPS,
+            "select_groups_us": t_sel * 1e3, "active_set_us": t_act * 1e3,
+            "kv_update_us": t_kv * 1e3, "kv_update_gbs": kv_bytes / t_kv / 1e6,
+            "euler_us": t_eu * 1e3, "euler_gbs": eu_bytes / t_eu / 1e6})
+        print(f"bench: sweep f={f} attention {flops / t_att / 1e9:.0f} TFLOP/s", file=sys.stderr,
+              flush=True)
+    return out
 
 
 def main():
@@ -297,6 +359,9 @@ def main():
     if args.loop:
         print("bench: full schedule loop", file=sys.stderr, flush=True)
         res["full_schedule"] = run_loop(hs, synth, torch)
+    if args.sweep:
+        print("bench: large-head sweep", file=sys.stderr, flush=True)
+        res["large_head_sweep"] = run_sweep(hs, synth, torch)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
