@@ -87,8 +87,11 @@ int hsastep_n_active(int64_t n_tokens, const int32_t* budgets_host,
  *   v_prev, v_cur      [n_tokens, channels] fp32
  *   group_sizes_host   [n_groups] host int64, each >= 0, summing to n_tokens
  *   group_id           [n_tokens] int32 output, values in [0, n_groups)
- *   score_or_null      [n_tokens] fp32 output r, or NULL
- *   workspace          >= hsastep_workspace_bytes(n_tokens, n_groups) bytes
+ *   score_or_null      [n_tokens] fp32 output r, or NULL (r then stays in the workspace)
+ *   workspace          device buffer, 16-byte aligned, of at least
+ *                      hsastep_workspace_bytes(n_tokens, n_groups) bytes; always
+ *                      required (it holds the grouping histograms); its contents
+ *                      on entry do not matter and are overwritten
  * Limits: 1 <= n_tokens <= 2^31 - 1, 1 <= channels <= HSASTEP_MAX_CHANNELS,
  *         1 <= n_groups <= HSASTEP_MAX_GROUPS.
  */

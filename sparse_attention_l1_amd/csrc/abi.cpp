@@ -89,12 +89,11 @@ HSASTEP_API int hsa_select_groups(const float* v_prev, const float* v_cur, int64
   }
   if (total != n_tokens) return fail(HSASTEP_ERR_ARG, "group sizes must sum to n_tokens");
   const hsastep::WorkspaceLayout wl = hsastep::workspace_layout(n_tokens, n_groups);
-  float* r = score_or_null;
-  if (r == nullptr) {
-    if (workspace == nullptr || workspace_bytes < wl.total)
-      return fail(HSASTEP_ERR_WORKSPACE, "workspace smaller than hsastep_workspace_bytes()");
-    r = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.score_off);
-  }
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(HSASTEP_ERR_WORKSPACE, "workspace smaller than hsastep_workspace_bytes()");
+  if (!aligned16(workspace)) return fail(HSASTEP_ERR_ARG, "workspace must be 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  float* r = score_or_null ? score_or_null : reinterpret_cast<float*>(ws + wl.score_off);
   // first rank of each later group; ranks >= n_tokens never occur, so drop those targets
   int64_t targets[HSASTEP_MAX_GROUPS];
   int nt = 0;
@@ -103,10 +102,13 @@ HSASTEP_API int hsa_select_groups(const float* v_prev, const float* v_cur, int64
     cum += group_sizes_host[k];
     if (cum < n_tokens) targets[nt++] = cum;
   }
+  uint32_t* rank_ws = reinterpret_cast<uint32_t*>(ws + wl.rank_off);
+  const int64_t zero_words = nt > 0 ? int64_t(hsastep::rank_workspace(n_tokens, nt).zero_words) : 0;
   hipStream_t s = as_stream(stream);
-  if (int rc = hip_status(hsastep::launch_score(v_prev, v_cur, n_tokens, channels, r, s), "score"))
+  if (int rc = hip_status(hsastep::launch_score(v_prev, v_cur, n_tokens, channels, r, rank_ws,
+                                                zero_words, s), "score"))
     return rc;
-  return hip_status(hsastep::launch_rank(r, n_tokens, targets, nt, group_id, s), "rank");
+  return hip_status(hsastep::launch_rank(r, n_tokens, targets, nt, rank_ws, group_id, s), "rank");
 }
 
 HSASTEP_API int hsa_active_set(const int32_t* group_id, int64_t n_tokens,

@@ -73,7 +73,31 @@ int64_t n_active_from_mask(uint32_t mask, const int64_t* sizes, int32_t n_groups
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t /*n_groups*/) {
+int64_t rank_tokens_per_block(int64_t n_tokens) {
+  const int64_t chunks = n_tokens > 0 ? (n_tokens + kRankChunk - 1) / kRankChunk : 1;
+  const int64_t blocks = chunks < kRankMaxBlocks ? chunks : kRankMaxBlocks;
+  return kRankChunk * ((chunks + blocks - 1) / blocks);
+}
+
+int64_t rank_blocks(int64_t n_tokens) {
+  const int64_t per = rank_tokens_per_block(n_tokens);
+  const int64_t b = n_tokens > 0 ? (n_tokens + per - 1) / per : 1;
+  return b;
+}
+
+RankWorkspace rank_workspace(int64_t n_tokens, int n_targets) {
+  RankWorkspace w{};
+  const size_t nt = n_targets > 0 ? size_t(n_targets) : 0;
+  w.hist0_off = 0;
+  w.hist1_off = w.hist0_off + 2048;
+  w.hist2_off = w.hist1_off + nt * 2048;
+  w.block2_off = w.hist2_off + nt * 1024;
+  w.zero_words = w.block2_off;
+  w.total_words = w.block2_off + size_t(rank_blocks(n_tokens)) * nt * 1024;
+  return w;
+}
+
+WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_groups) {
   WorkspaceLayout w{};
   const size_t n = n_tokens > 0 ? size_t(n_tokens) : 0;
   w.score_off = 0;
@@ -81,7 +105,10 @@ WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t /*n_groups*/) {
   w.blockcnt_off = w.score_off + w.score_bytes;
   const size_t nblk = (n + kActiveBlockTokens - 1) / kActiveBlockTokens;
   w.blockcnt_bytes = align256((nblk + 1) * sizeof(int32_t));
-  w.total = w.blockcnt_off + w.blockcnt_bytes;
+  w.rank_off = w.blockcnt_off + w.blockcnt_bytes;
+  const int nt = n_groups > 1 ? n_groups - 1 : 0;
+  w.rank_bytes = align256(rank_workspace(n_tokens, nt).total_words * sizeof(uint32_t));
+  w.total = w.rank_off + w.rank_bytes;
   return w;
 }
 

@@ -16,6 +16,21 @@ namespace hsastep {
 constexpr int kMaxGroups = 16;
 constexpr int kMaxChannels = 256;
 constexpr int kActiveBlockTokens = 1024;   // tokens per workgroup of the active-set kernels
+constexpr int kRankThreads = 256;          // threads per workgroup of the grouping kernels
+constexpr int kRankChunk = 2048;           // tokens a grouping workgroup holds at once
+constexpr int kRankMaxBlocks = 512;        // cap on grouping workgroups (bounds the workspace)
+
+// Grouping kernels: tokens per workgroup (a multiple of kRankChunk) and workgroups.
+int64_t rank_tokens_per_block(int64_t n_tokens);
+int64_t rank_blocks(int64_t n_tokens);
+
+// Grouping workspace, offsets in uint32 words from its start: the three global
+// radix histograms (zeroed before each selection; they are contiguous, zero_words
+// long) and every workgroup's own pass-2 counts.
+struct RankWorkspace {
+  size_t hist0_off, hist1_off, hist2_off, block2_off, zero_words, total_words;
+};
+RankWorkspace rank_workspace(int64_t n_tokens, int n_targets);
 
 // Validates budgets / sizes / T / m for n_groups groups over n_tokens tokens.
 // Returns 0 or -1 with a message.  Budgets must start with T, divide T and be
@@ -34,6 +49,7 @@ int64_t n_active_from_mask(uint32_t mask, const int64_t* sizes, int32_t n_groups
 struct WorkspaceLayout {
   size_t score_off, score_bytes;        // fp32 [N] scores when the caller passes none
   size_t blockcnt_off, blockcnt_bytes;  // int32 [ceil(N / 1024)] per-workgroup active counts
+  size_t rank_off, rank_bytes;          // uint32 grouping histograms (RankWorkspace)
   size_t total;
 };
 WorkspaceLayout workspace_layout(int64_t n_tokens, int32_t n_groups);

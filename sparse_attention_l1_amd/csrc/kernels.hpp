@@ -8,14 +8,16 @@
 
 namespace hsastep {
 
-// score.hip: r[n] = L1 relative change of token n (balanced-tree fp32 sums).
+// score.hip: r[n] = L1 relative change of token n (balanced-tree fp32 sums); the
+// same launch also sets zero[0 .. zero_words) to 0 (the grouping histograms).
 hipError_t launch_score(const float* v_prev, const float* v_cur, int64_t n_tokens, int channels,
-                        float* r, hipStream_t stream);
+                        float* r, uint32_t* zero, int64_t zero_words, hipStream_t stream);
 
 // rank.hip: group id from the rank of r (largest first, ties by index).
 // targets[t] = first rank of group t+1 (only targets < n_tokens are passed).
+// rank_ws: the grouping workspace (RankWorkspace), its histograms already zero.
 hipError_t launch_rank(const float* r, int64_t n_tokens, const int64_t* targets, int n_targets,
-                       int32_t* group_id, hipStream_t stream);
+                       uint32_t* rank_ws, int32_t* group_id, hipStream_t stream);
 
 // active.hip: ascending active index list + inverse map for one iteration.
 hipError_t launch_active(const int32_t* group_id, int64_t n_tokens, uint32_t group_mask,

@@ -23,9 +23,12 @@ template <int P, bool kVec4>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ v_prev,
                                                     const float* __restrict__ v_cur,
                                                     int64_t n_tokens, int channels,
-                                                    float* __restrict__ r) {
+                                                    float* __restrict__ r,
+                                                    uint32_t* __restrict__ zero,
+                                                    int64_t zero_words) {
 #pragma clang fp contract(off)
   const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = tid; i < zero_words; i += int64_t(gridDim.x) * blockDim.x) zero[i] = 0u;
   const int64_t token = tid / P;
   const int lane = int(tid % P);
   // groups of P lanes are aligned inside a wavefront, so a whole group leaves together
@@ -77,33 +80,34 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ v_
 }
 
 template <int P>
-hipError_t launch_p(const float* vp, const float* vc, int64_t n, int ch, float* r, hipStream_t s) {
+hipError_t launch_p(const float* vp, const float* vc, int64_t n, int ch, float* r, uint32_t* z,
+                    int64_t zw, hipStream_t s) {
   const int64_t threads = n * P;
   const int block = 256;
   const int64_t grid = (threads + block - 1) / block;
   if (ch % 4 == 0)
-    score_kernel<P, true><<<dim3(unsigned(grid)), dim3(block), 0, s>>>(vp, vc, n, ch, r);
+    score_kernel<P, true><<<dim3(unsigned(grid)), dim3(block), 0, s>>>(vp, vc, n, ch, r, z, zw);
   else
-    score_kernel<P, false><<<dim3(unsigned(grid)), dim3(block), 0, s>>>(vp, vc, n, ch, r);
+    score_kernel<P, false><<<dim3(unsigned(grid)), dim3(block), 0, s>>>(vp, vc, n, ch, r, z, zw);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_score(const float* v_prev, const float* v_cur, int64_t n_tokens, int channels,
-                        float* r, hipStream_t stream) {
+                        float* r, uint32_t* zero, int64_t zero_words, hipStream_t stream) {
   // lanes per token: next power of two of ceil(C/4), at least 1, at most 64 (C <= 256)
   const int need = (channels + 3) / 4;
   int p = 1;
   while (p < need) p <<= 1;
   switch (p) {
-    case 1: return launch_p<1>(v_prev, v_cur, n_tokens, channels, r, stream);
-    case 2: return launch_p<2>(v_prev, v_cur, n_tokens, channels, r, stream);
-    case 4: return launch_p<4>(v_prev, v_cur, n_tokens, channels, r, stream);
-    case 8: return launch_p<8>(v_prev, v_cur, n_tokens, channels, r, stream);
-    case 16: return launch_p<16>(v_prev, v_cur, n_tokens, channels, r, stream);
-    case 32: return launch_p<32>(v_prev, v_cur, n_tokens, channels, r, stream);
-    default: return launch_p<64>(v_prev, v_cur, n_tokens, channels, r, stream);
+    case 1: return launch_p<1>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
+    case 2: return launch_p<2>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
+    case 4: return launch_p<4>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
+    case 8: return launch_p<8>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
+    case 16: return launch_p<16>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
+    case 32: return launch_p<32>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
+    default: return launch_p<64>(v_prev, v_cur, n_tokens, channels, r, zero, zero_words, stream);
   }
 }
 

@@ -111,19 +111,16 @@ def workspace(n_tokens: int, n_groups: int, device="cuda") -> torch.Tensor:
 
 
 def hsa_select_groups(v_prev: torch.Tensor, v_cur: torch.Tensor, group_sizes: Sequence[int],
-                      group_id: torch.Tensor, score: Optional[torch.Tensor] = None,
-                      ws: Optional[torch.Tensor] = None, stream=None) -> None:
+                      group_id: torch.Tensor, score: Optional[torch.Tensor],
+                      ws: torch.Tensor, stream=None) -> None:
     n, c = v_prev.shape
     if v_cur.shape != v_prev.shape or group_id.shape != (n,):
         raise ValueError("shape mismatch")
-    if score is None and ws is None:
-        raise ValueError("pass a score output or a workspace")
     _check(lib.hsa_select_groups(
         _dev(v_prev, "v_prev", (torch.float32,)), _dev(v_cur, "v_cur", (torch.float32,)), n, c,
         _host_i64(group_sizes), len(group_sizes), _dev(group_id, "group_id", (torch.int32,)),
         None if score is None else _dev(score, "score", (torch.float32,)),
-        None if ws is None else _dev(ws, "workspace", (torch.uint8,)),
-        0 if ws is None else ws.numel(), _stream(stream)), "hsa_select_groups")
+        _dev(ws, "workspace", (torch.uint8,)), ws.numel(), _stream(stream)), "hsa_select_groups")
 
 
 def hsa_active_set(group_id: torch.Tensor, budgets: Sequence[int], group_sizes: Sequence[int],

@@ -71,7 +71,7 @@ class HsaSampler:
             self.v_cache[l].copy_(v)
 
     def select(self, v_prev: torch.Tensor, v_cur: torch.Tensor) -> None:
-        hs.hsa_select_groups(v_prev, v_cur, self.sizes, self.group_id, self.score)
+        hs.hsa_select_groups(v_prev, v_cur, self.sizes, self.group_id, self.score, self.ws)
 
     def active_set(self, i: int) -> int:
         self.n_active = hs.hsa_active_set(self.group_id, self.budgets, self.sizes, self.T, self.m, i,

@@ -74,8 +74,11 @@ def test_select_groups_rejects(hs):
     assert f(None, FAKE, 10, 16, sizes, 2, FAKE, FAKE, FAKE, ws, None) == hs.ERR_ARG
     assert f(ctypes.c_void_p((1 << 20) + 4), FAKE, 10, 16, sizes, 2, FAKE, FAKE, FAKE, ws,
              None) == hs.ERR_ARG
-    # no score output and no / too small workspace
+    # no / too small workspace, with or without a score output
     assert f(FAKE, FAKE, 10, 16, sizes, 2, FAKE, None, None, 0, None) == hs.ERR_WORKSPACE
+    assert f(FAKE, FAKE, 10, 16, sizes, 2, FAKE, FAKE, None, ws, None) == hs.ERR_WORKSPACE
+    assert f(FAKE, FAKE, 10, 16, sizes, 2, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 8), ws,
+             None) == hs.ERR_ARG
     assert f(FAKE, FAKE, 10, 16, sizes, 2, FAKE, None, FAKE, ws - 1, None) == hs.ERR_WORKSPACE
     assert f(FAKE, FAKE, 10, 16, bad_sizes, 2, FAKE, FAKE, FAKE, ws, None) == hs.ERR_ARG
     assert b"sum to n_tokens" in hs.lib.hsastep_last_error()

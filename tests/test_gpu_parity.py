@@ -45,6 +45,11 @@ def velocities(kind, n, c, seed):
     if kind == "ties":
         vp = np.ones((n, c), np.float32)
         return vp, (vp * np.float32(1.25)).astype(np.float32)
+    if kind == "levels":
+        # r is exactly one of 4 values: long runs of equal keys across many workgroups
+        vp = np.ones((n, c), np.float32)
+        lv = np.array([0.0, 0.5, 1.0, 2.0], np.float32)[r.integers(0, 4, n)]
+        return vp, (vp + lv[:, None]).astype(np.float32)
     if kind == "heavy":
         lam = np.abs(r.standard_t(3, n)).astype(np.float32)
     else:
@@ -68,6 +73,9 @@ SELECT_CASES = [
     ("ties", 2500, 16, (700, 1100, 700)),
     ("heavy", 75600, 64, (7560, 22680, 45360)),
     ("lognormal", 32760, 64, (16380, 16380)),
+    ("ties", 20000, 4, (3000, 9000, 8000)),
+    # more than 512 chunks of 2048 tokens: workgroups then hold 4096 tokens each
+    ("levels", 1100000, 1, (100000, 350000, 0, 650000)),
     ("lognormal", 4097, 255, tuple([256] * 15 + [257])),
     ("lognormal", 333, 1, (100, 233)),
 ]
@@ -79,7 +87,7 @@ def test_select_groups(hs, kind, n, c, sizes):
     g_want, r_want = oracle.select_groups(vp, vc, sizes)
     g = torch.full((n,), -5, dtype=torch.int32, device="cuda")
     r = torch.empty(n, dtype=torch.float32, device="cuda")
-    hs.hsa_select_groups(dev(vp), dev(vc), sizes, g, r)
+    hs.hsa_select_groups(dev(vp), dev(vc), sizes, g, r, hs.workspace(n, len(sizes)))
     # the workspace variant (no score output) gives the same groups
     g2 = torch.full((n,), -5, dtype=torch.int32, device="cuda")
     hs.hsa_select_groups(dev(vp), dev(vc), sizes, g2, None, hs.workspace(n, len(sizes)))
