@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of one HSA denoise iteration on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--loop]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--loop] [--pair]
+                    [--sweep]
 
 A step is one pass of the whole path over the single-step workload (N = 32760
 tokens on a 21x30x52 latent grid, 12 heads x 128, 64 latent channels, half of
@@ -14,7 +15,9 @@ value = attention FLOPs of the iteration (4 * |A| * N * H * D) / wall time of th
 whole iteration, in TFLOP/s; ms_per_step is that wall time.  The roofline entry
 is the attention kernel alone, timed with HIP events around each launch.
 With --loop the full 40-iteration, 30-layer schedule (T=40, budgets {40,20,10,5},
-m=4) is also run once and its mean ms per iteration reported.
+m=4) is also run once and its mean ms per iteration reported; --pair does the same for
+the aggressive cond/uncond pair (B=2, N=75600, 40x128 heads, 40 layers, T=40, budgets
+{40,10,5} over 10/30/60% of the tokens, m=2).
 """
 from __future__ import annotations
 
@@ -44,6 +47,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--loop", action="store_true", help="also time the full 40-iteration schedule")
+    p.add_argument("--pair", action="store_true",
+                   help="also run the aggressive cond/uncond pair: B=2, N=75600, 40x128 heads, "
+                        "40 layers, T=40 {40,10,5} over 10/30/60%%, m=2 (~2-3 minutes, 124 GB "
+                        "of caches)")
     p.add_argument("--sweep", action="store_true",
                    help="also time the large-head sweep: N=75600, 40x128 heads, active fraction "
                         "1, 1/2, 1/4, 1/8 (attention, selection, scatter, Euler per kernel)")
@@ -186,24 +193,27 @@ def cpu_baseline(budget_s: float):
                        f"extrapolated step {t_step:.1f} s")}
 
 
-def run_loop(hs, synth, torch):
-    """Full 40-iteration schedule, 30 layers (T=40, budgets {40,20,10,5}, m=4): mean ms per
-    iteration of the whole path with the synthetic model stand-in (pool windows on device)."""
+def run_loop(hs, synth, torch, cfg):
+    """A whole sampling run (all T iterations, every layer) through the C ABI with the synthetic
+    model stand-in (seeded Q/K/V pool windows and velocities, on the device): ms per iteration
+    (HIP events around each), and the attention FLOPs of the run over its wall time."""
     from sparse_attention_l1_amd.sampler import HsaSampler
-    cfg = synth.full_schedule()
     dev = torch.device("cuda")
-    N, C, H, D = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim
+    N, C, H, D, B = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim, cfg.batch
     src = synth.QKVSource(cfg)
     vm = synth.VelocityModel(cfg)
     pools = {t: torch.from_numpy(src.pools[t].bits.view(np.int16)).to(dev) for t in "qkv"}
     pre = torch.from_numpy(src.prefill(0).view(np.int16)).to(dev)
+    del src.prefill_pool
     v_all = [torch.from_numpy(vm(i)).to(dev) for i in range(cfg.T)]
 
     class PoolModel:
         def qkv(self, l, i, active_idx, na):
             need = na * H * D
-            return tuple(pools[t][src.pools[t].offset(need, 0, l, i):][:need].view(1, na, H, D)
-                         for t in "qkv")
+            wins = lambda t: [pools[t][src.pools[t].offset(need, b, l, i):][:need] for b in range(B)]
+            if B == 1:
+                return tuple(wins(t)[0].view(1, na, H, D) for t in "qkv")
+            return tuple(torch.stack(wins(t)).view(B, na, H, D) for t in "qkv")
 
         def velocity(self, i, active_idx, na):
             out = vbuf[:na]
@@ -211,7 +221,7 @@ def run_loop(hs, synth, torch):
             return out
 
     vbuf = torch.empty((N, C), dtype=torch.float32, device=dev)
-    smp = HsaSampler(n_tokens=N, channels=C, batch=1, heads=H, head_dim=D, layers=cfg.layers,
+    smp = HsaSampler(n_tokens=N, channels=C, batch=B, heads=H, head_dim=D, layers=cfg.layers,
                      T=cfg.T, budgets=cfg.budgets, group_sizes=cfg.sizes, m=cfg.m)
     smp.reset(torch.from_numpy(synth.latent0(cfg)).to(dev), torch.from_numpy(vm.v_prev).to(dev),
               lambda l: (pre, pre))
@@ -225,13 +235,18 @@ def run_loop(hs, synth, torch):
         evs[i][0].record()
         smp.iteration(i, model)
         evs[i][1].record()
-        flops += 4.0 * smp.n_active * N * H * D * cfg.layers
+        flops += 4.0 * B * smp.n_active * N * H * D * cfg.layers
+        if B > 1 or cfg.layers > 30:
+            torch.cuda.synchronize()   # long iterations: report progress as they finish
+            print(f"bench: {cfg.name}: iteration {i} done, |A| = {smp.n_active}", file=sys.stderr,
+                  flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_iter = [a.elapsed_time(b) for a, b in evs]
-    return {"workload": cfg.name, "iterations": cfg.T, "layers": cfg.layers,
+    return {"workload": cfg.name, "iterations": cfg.T, "layers": cfg.layers, "batch": B,
             "ms_per_iteration_mean": float(np.mean(per_iter)),
             "ms_per_iteration": [round(x, 3) for x in per_iter],
+            "ms_total": float(np.sum(per_iter)),
             "attention_pflop": flops / 1e15, "tflops_effective": flops / wall / 1e12,
             "wall_s": wall}
 
@@ -358,7 +373,10 @@ def main():
     }
     if args.loop:
         print("bench: full schedule loop", file=sys.stderr, flush=True)
-        res["full_schedule"] = run_loop(hs, synth, torch)
+        res["full_schedule"] = run_loop(hs, synth, torch, synth.full_schedule())
+    if args.pair:
+        print("bench: aggressive pair loop", file=sys.stderr, flush=True)
+        res["aggressive_pair"] = run_loop(hs, synth, torch, synth.aggressive_pair())
     if args.sweep:
         print("bench: large-head sweep", file=sys.stderr, flush=True)
         res["large_head_sweep"] = run_sweep(hs, synth, torch)

@@ -24,6 +24,8 @@ from __future__ import annotations
 import dataclasses
 from typing import Optional, Tuple
 
+import concurrent.futures
+
 import numpy as np
 
 SEED = 20260512
@@ -112,9 +114,14 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
     Inputs are finite; this is a storage-format conversion of generated data.
     """
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
-    return r.astype(np.uint16)
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    out = np.empty(u.shape, np.uint16)
+    flat_u, flat_o = u.reshape(-1), out.reshape(-1)
+    step = 1 << 24   # chunks bound the temporaries; finite inputs cannot overflow uint32 here
+    for s in range(0, flat_u.size, step):
+        c = flat_u[s:s + step]
+        flat_o[s:s + step] = (c + np.uint32(0x7FFF) + ((c >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return out
 
 
 def splitmix64(x: int) -> int:
@@ -214,9 +221,13 @@ class QKVSource:
         rows = cfg.n_tokens if max_rows is None else max_rows
         row = cfg.heads * cfg.head_dim
         need = rows * row
-        self.pools = {t: Pool(cfg.cfg_id, s, pool_length(need))
-                      for t, s in (("q", STREAM_Q), ("k", STREAM_K), ("v", STREAM_V))}
-        self.prefill_pool = Pool(cfg.cfg_id, STREAM_PREFILL, pool_length(cfg.n_tokens * row))
+        jobs = [("q", STREAM_Q, need), ("k", STREAM_K, need), ("v", STREAM_V, need),
+                ("prefill", STREAM_PREFILL, cfg.n_tokens * row)]
+        # the four pools are independent seeded streams: generate them concurrently
+        with concurrent.futures.ThreadPoolExecutor(len(jobs)) as ex:
+            made = list(ex.map(lambda j: Pool(cfg.cfg_id, j[1], pool_length(j[2])), jobs))
+        self.pools = {j[0]: p for j, p in zip(jobs[:3], made[:3])}
+        self.prefill_pool = made[3]
 
     def rows(self, tensor: str, layer: int, i: int, n_rows: int) -> np.ndarray:
         c = self.cfg

@@ -38,9 +38,18 @@ class SyntheticModel:
         self.cfg, self.hs = cfg, hs
         self.src = synth.QKVSource(cfg)
         self.vm = synth.VelocityModel(cfg)
+        # the pools on the device: a (tensor, b, layer, i) window is then a device slice
+        self.pools = {t: bits_dev(self.src.pools[t].bits) for t in ("q", "k", "v")}
 
     def qkv(self, l, i, active_idx, na):
-        return tuple(bits_dev(self.src.rows(t, l, i, na)) for t in ("q", "k", "v"))
+        c = self.cfg
+        need = na * c.heads * c.head_dim
+        out = []
+        for t in ("q", "k", "v"):
+            wins = [self.pools[t][self.src.pools[t].offset(need, b, l, i):][:need]
+                    for b in range(c.batch)]
+            out.append(torch.stack(wins).view(c.batch, na, c.heads, c.head_dim))
+        return tuple(out)
 
     def velocity(self, i, active_idx, na):
         full = dev(self.vm(i))

@@ -326,3 +326,75 @@ def test_single_step_full_size(hs):
     xw, vw = oracle.euler_step(x0, vhat0, model.vm(i)[idx_w], idx_w, sig[i], sig[i + 1])
     assert np.array_equal(host(vhd), vw)
     assert np.array_equal(host(xd).view(np.uint32), xw.view(np.uint32))
+
+
+def test_aggressive_pair_full_size_loop(hs):
+    """B = 2 (a cond/uncond pair), N = 75600, 40 x 128 heads, T = 40, budgets {40, 10, 5} over
+    10/30/60% of the tokens, heavy-tailed drift, m = 2, one layer: the whole 40-iteration loop
+    through the C ABI.  Active sets, group ids, the latent and the velocity cache are compared
+    in full at every iteration.  At iteration 37 (10% of the tokens active, so most cache rows
+    are stale) sampled cache rows are compared with the replay rule (a row holds the K/V of the
+    last iteration that had its token active, else the prefill) and attention with the oracle
+    on sampled query rows, the oracle's caches rebuilt by that rule."""
+    from sparse_attention_l1_amd.sampler import HsaSampler
+    cfg = synth.aggressive_pair()
+    N, H, D, T, B = cfg.n_tokens, cfg.heads, cfg.head_dim, cfg.T, cfg.batch
+    check_i = 37
+    model = SyntheticModel(cfg, hs)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    rec = {}
+    oracle.run_hsa(synth.latent0(cfg), model.vm.v_prev, model.vm, model.src.rows,
+                   model.src.prefill, T=T, budgets=cfg.budgets, group_sizes=cfg.sizes, m=cfg.m,
+                   layers=0, scale=scale,
+                   record=lambda i, s: rec.__setitem__(i, {k: s[k] for k in
+                                                           ("active_idx", "group_id", "x", "v_hat")}))
+    assert rec[check_i]["active_idx"].shape[0] == cfg.sizes[0]
+    smp = HsaSampler(n_tokens=N, channels=cfg.channels, batch=B, heads=H, head_dim=D, layers=1,
+                     T=T, budgets=cfg.budgets, group_sizes=cfg.sizes, m=cfg.m, softmax_scale=scale)
+    smp.reset(dev(synth.latent0(cfg)), dev(model.vm.v_prev), model.prefill)
+    qrows = synth.sample_rows(cfg.cfg_id, cfg.sizes[0], 24, tag=1)
+    crow = synth.sample_rows(cfg.cfg_id, N, 256, tag=2)
+    got = {}
+
+    def observe(l, o):
+        if smp_i[0] == check_i:
+            got["attn"] = host_bits(o[:, torch.from_numpy(qrows).cuda()])
+            got["k"] = host_bits(smp.k_cache[0][:, torch.from_numpy(crow).cuda()])
+            got["v"] = host_bits(smp.v_cache[0][:, torch.from_numpy(crow).cuda()])
+
+    smp_i = [0]
+    for i in range(T):
+        smp_i[0] = i
+        smp.iteration(i, model, on_attention=observe)
+        torch.cuda.synchronize()
+        want = rec[i]
+        na = smp.n_active
+        print(f"[pair loop] iteration {i}: {na} active", flush=True)
+        assert na == want["active_idx"].shape[0], f"iteration {i}"
+        assert np.array_equal(host(smp.active_idx)[:na], want["active_idx"]), f"iteration {i}"
+        assert np.array_equal(host(smp.group_id), want["group_id"]), f"iteration {i}"
+        assert np.array_equal(host(smp.v_hat), want["v_hat"]), f"iteration {i}"
+        assert np.array_equal(host(smp.x).view(np.uint32), want["x"].view(np.uint32)), f"iteration {i}"
+
+    # replay rule for layer 0 after the scatter of iteration check_i
+    last = np.full(N, -1, np.int64)
+    pos = np.zeros(N, np.int64)
+    for j in range(check_i + 1):
+        idx = rec[j]["active_idx"]
+        last[idx] = j
+        pos[idx] = np.arange(idx.shape[0])
+    caches = {}
+    for t in ("k", "v"):
+        c = model.src.prefill(0)
+        for j in np.unique(last[last >= 0]):
+            toks = np.flatnonzero(last == j)
+            need = rec[j]["active_idx"].shape[0] * H * D
+            for b in range(B):
+                win = model.src.pools[t].window(need, b, 0, j).reshape(-1, H, D)
+                c[b, toks] = win[pos[toks]]
+        caches[t] = c
+        assert np.array_equal(got[t], c[:, crow]), f"cache {t} rows at iteration {check_i}"
+    na = rec[check_i]["active_idx"].shape[0]
+    q = model.src.rows("q", 0, check_i, na)[:, qrows]
+    want = oracle.attention_active(q, caches["k"], caches["v"], scale)
+    attn_close(got["attn"], want, f"pair loop i{check_i} sampled rows")
