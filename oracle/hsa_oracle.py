@@ -31,6 +31,10 @@ Readings taken where the pages are silent (each marked READING below):
      velocities with the velocity cache before the Euler write (for m = 0 the
      caller supplies (v_prev, v_cur) and selects before iteration 0).
   R10 cache slot = token index; scatter precedes attention in every layer.
+  R11 variant (run_hsa(reselect=True)), the fuller reading of dynamic selection:
+     besides the selection of R9, the groups are recomputed the same way at every
+     later iteration in which every token is active (|A_i| = N), from the velocity
+     cache and that iteration's fresh velocities, before the Euler write.
 """
 from __future__ import annotations
 
@@ -215,7 +219,7 @@ def euler_step(x: np.ndarray, v_hat: np.ndarray, v_fresh: np.ndarray, active_idx
 
 
 def run_hsa(x0, v_prev, velocity, qkv, prefill, *, T, budgets, group_sizes, m, layers, scale,
-            v_cur_for_m0=None, record=None):
+            v_cur_for_m0=None, record=None, reselect=False):
     """The full HSA sampling loop, iteration by iteration ([HSA-nl §2.1-§2.4]).
 
     velocity(i) -> [N, C] float32: the model's velocity prediction at iteration i
@@ -224,6 +228,7 @@ def run_hsa(x0, v_prev, velocity, qkv, prefill, *, T, budgets, group_sizes, m, l
         the projections of the active tokens, in active_idx order.
     prefill(layer) -> [B, N, H, D] bf16 bits: the cache content before iteration 0.
     record(i, state: dict): optional observer called at the end of every iteration.
+    reselect: READING R11, regroup at every all-active iteration after the first selection.
 
     Returns the final (x, v_hat, group_id, k_caches, v_caches).
     """
@@ -247,8 +252,8 @@ def run_hsa(x0, v_prev, velocity, qkv, prefill, *, T, budgets, group_sizes, m, l
             outs.append(attention_active(qkv("q", l, i, na), kc[l], vc[l], scale))
         v_fresh = np.asarray(velocity(i), dtype=np.float32)[active_idx]
         r = None
-        if m >= 1 and i == sel_iter:
-            # all tokens are active here (i < m), so v_fresh is in token order
+        if (m >= 1 and i == sel_iter) or (reselect and na == n and i >= sel_iter):
+            # all tokens are active here, so v_fresh is in token order
             g, r = select_groups(v_hat, v_fresh, group_sizes)
         x, v_hat = euler_step(x, v_hat, v_fresh, active_idx, sig[i], sig[i + 1])
         if record is not None:

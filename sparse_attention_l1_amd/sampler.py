@@ -9,7 +9,8 @@ Staptoewijzing (HSA) voor Efficiënte Videogeneratie", §2.1-§2.4):
                 hsa_kv_update         fresh K/V rows overwrite their cache slots
                 hsa_attention_active  active queries x all N cached rows
     model(A_i) -> fresh velocities of the active tokens
-    (once, at iteration max(m,1)-1, where every token is active)
+    (at iteration max(m,1)-1, where every token is active; with reselect=True also
+     at every later iteration in which every token is active)
                 hsa_select_groups     groups by L1 relative velocity change
     hsa_euler_step          cached Euler update of all N latents
 
@@ -36,7 +37,7 @@ def sigma_schedule(T: int) -> np.ndarray:
 class HsaSampler:
     def __init__(self, *, n_tokens: int, channels: int, batch: int, heads: int, head_dim: int,
                  layers: int, T: int, budgets: Sequence[int], group_sizes: Sequence[int], m: int,
-                 softmax_scale: Optional[float] = None, device="cuda"):
+                 softmax_scale: Optional[float] = None, device="cuda", reselect: bool = False):
         self.N, self.C, self.B, self.H, self.D, self.L = n_tokens, channels, batch, heads, head_dim, layers
         self.T, self.budgets, self.sizes, self.m = T, list(budgets), list(group_sizes), m
         self.scale = float(np.float32(1.0 / np.sqrt(head_dim))) if softmax_scale is None else softmax_scale
@@ -58,6 +59,7 @@ class HsaSampler:
         self.attn_out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
         self.n_active = n_tokens
         self.selection_iter = max(m, 1) - 1
+        self.reselect = reselect
 
     def reset(self, x0: torch.Tensor, v_prev: torch.Tensor,
               prefill: Callable[[int], Sequence[torch.Tensor]]) -> None:
@@ -98,7 +100,9 @@ class HsaSampler:
             if on_attention is not None:
                 on_attention(l, out)
         v_fresh = model.velocity(i, self.active_idx, na)
-        if self.m >= 1 and i == self.selection_iter:
-            # every token is active inside the window, so v_fresh is in token order
+        regroup = self.m >= 1 and i == self.selection_iter
+        regroup |= self.reselect and na == self.N and i >= self.selection_iter
+        if regroup:
+            # every token is active here, so v_fresh is in token order
             self.select(self.v_hat, v_fresh)
         self.euler(i, v_fresh)

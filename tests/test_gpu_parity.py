@@ -235,7 +235,7 @@ def test_euler(hs, N, C, frac):
 
 # ----------------------------------------------------------------------------- whole loop
 
-def run_loop_both(cfg, hs, layers=None):
+def run_loop_both(cfg, hs, layers=None, reselect=False):
     from sparse_attention_l1_amd.sampler import HsaSampler
     L = cfg.layers if layers is None else layers
     model = SyntheticModel(cfg, hs)
@@ -243,10 +243,11 @@ def run_loop_both(cfg, hs, layers=None):
     rec = {}
     oracle.run_hsa(synth.latent0(cfg), model.vm.v_prev, model.vm, model.src.rows, model.src.prefill,
                    T=cfg.T, budgets=cfg.budgets, group_sizes=cfg.sizes, m=cfg.m, layers=L,
-                   scale=scale, v_cur_for_m0=model.vm(0), record=lambda i, s: rec.__setitem__(i, s))
+                   scale=scale, v_cur_for_m0=model.vm(0), record=lambda i, s: rec.__setitem__(i, s),
+                   reselect=reselect)
     smp = HsaSampler(n_tokens=cfg.n_tokens, channels=cfg.channels, batch=cfg.batch, heads=cfg.heads,
                      head_dim=cfg.head_dim, layers=L, T=cfg.T, budgets=cfg.budgets,
-                     group_sizes=cfg.sizes, m=cfg.m, softmax_scale=scale)
+                     group_sizes=cfg.sizes, m=cfg.m, softmax_scale=scale, reselect=reselect)
     smp.reset(dev(synth.latent0(cfg)), dev(model.vm.v_prev), model.prefill)
     if cfg.m == 0:
         smp.select(dev(model.vm.v_prev), dev(model.vm(0)))
@@ -281,6 +282,18 @@ def test_small_loop_three_groups_two_layers_pair(hs):
 def test_small_loop_no_window(hs):
     cfg = synth.Config("m0", 78, 300, 16, 1, 1, 64, 1, 4, (4, 2, 1), (50, 50, 200), 0)
     run_loop_both(cfg, hs)
+
+
+def test_loop_reselect_at_every_all_active_iteration(hs):
+    # groups recomputed at i = 1, 4, 8, 12, 16 and the closing window 18, 19 (periods 1, 2, 4;
+    # m = 2)
+    cfg = synth.Config("reselect", 79, 700, 16, 2, 2, 64, 2, 20, (20, 10, 5), (100, 200, 400), 2,
+                       drift="student_t3")
+    run_loop_both(cfg, hs, reselect=True)
+
+
+def test_tiny_loop_reselect(hs):
+    run_loop_both(synth.tiny(), hs, reselect=True)
 
 
 def test_single_step_full_size(hs):

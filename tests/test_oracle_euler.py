@@ -151,3 +151,65 @@ def test_selection_happens_once_with_all_tokens_fresh():
     # the drift scale drives the split: the full-budget half holds the larger drifts
     lam = vm.lam
     assert np.median(lam[g0 == 0]) > np.median(lam[g0 == 1])
+
+
+# Regroup iterations with reselect=True, derived by hand from the schedule rule ([HSA-nl]
+# §2.1 periods T/s_k, §2.4 windows): every token is active iff i < m, i >= T - m, or i is a
+# multiple of every period; regrouping starts at the first selection, i = max(m,1) - 1.
+RESELECT_CASES = [
+    # T, m, budgets (periods), expected regroup iterations
+    (40, 4, (40, 20, 10, 5), [3, 8, 16, 24, 32, 36, 37, 38, 39]),   # periods 1,2,4,8
+    (40, 2, (40, 10, 5), [1, 8, 16, 24, 32, 38, 39]),               # periods 1,4,8
+    (8, 0, (8, 4), [0, 2, 4, 6]),                                   # no window, period 2
+    (12, 1, (12, 4, 3), [0, 11]),                                   # periods 1,3,4: lcm 12
+]
+
+
+@pytest.mark.parametrize("T,m,budgets,want", RESELECT_CASES)
+def test_reselect_regroups_at_every_all_active_iteration(T, m, budgets, want):
+    K = len(budgets)
+    sizes = tuple([10] * (K - 1) + [40 - 10 * (K - 1)])
+    cfg = synth.Config("reselect", 94, 40, 8, 1, 1, 64, 0, T, budgets, sizes, m)
+    vm = synth.VelocityModel(cfg)
+    rec = {}
+    oracle.run_hsa(synth.latent0(cfg), vm.v_prev, vm, None, None, T=T, budgets=budgets,
+                   group_sizes=sizes, m=m, layers=0, scale=0.125, v_cur_for_m0=vm(0),
+                   reselect=True, record=lambda i, s: rec.__setitem__(i, s))
+    got = [i for i in range(T) if rec[i]["score"] is not None]
+    assert got == want
+    g_prev = None
+    for i in range(T):
+        if i in want:
+            v_hat_before = vm.v_prev if i == 0 else rec[i - 1]["v_hat"]
+            assert rec[i]["active_idx"].shape[0] == cfg.n_tokens
+            g_want, _ = oracle.select_groups(v_hat_before, rec[i]["v_fresh"], sizes)
+            assert np.array_equal(rec[i]["group_id"], g_want)
+        elif g_prev is not None:
+            assert np.array_equal(rec[i]["group_id"], g_prev)
+        g_prev = rec[i]["group_id"]
+
+
+def test_reselect_follows_a_change_of_drift():
+    # drift scale of the first half 10x that of the second until iteration 8, then swapped:
+    # the regroup at i = 8 (periods 1, 2: every even i is all-active) moves the full budget
+    # to the second half, which the once-only selection does not
+    T, N = 16, 64
+    lam = np.where(np.arange(N) < N // 2, 1.0, 0.1).astype(np.float32)
+    r = np.random.default_rng(5)
+    v_prev = r.standard_normal((N, 8)).astype(np.float32)
+    z = [r.standard_normal((N, 8)).astype(np.float32) for _ in range(T)]
+    drift = np.zeros((N, 8), np.float32)
+    vel = []
+    for i in range(T):
+        scale = lam if i < 8 else lam[::-1]
+        drift = (drift + scale[:, None] * z[i]).astype(np.float32)
+        vel.append((v_prev + drift).astype(np.float32))
+    kw = dict(T=T, budgets=(16, 8), group_sizes=(N // 2, N // 2), m=1, layers=0, scale=0.125)
+    x0 = np.zeros((N, 8), np.float32)
+    _, _, g_once, _, _ = oracle.run_hsa(x0, v_prev, lambda i: vel[i], None, None, **kw)
+    rec = {}
+    _, _, g_re, _, _ = oracle.run_hsa(x0, v_prev, lambda i: vel[i], None, None, reselect=True,
+                                      record=lambda i, s: rec.__setitem__(i, s), **kw)
+    assert (g_once[: N // 2] == 0).mean() > 0.8          # selected at i = 0: first half fast
+    assert (rec[8]["group_id"][N // 2:] == 0).mean() > 0.8   # regrouped at i = 8: second half
+    assert (g_re[N // 2:] == 0).mean() > 0.8
