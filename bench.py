@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="also time the large-head sweep: N=75600, 40x128 heads, active fraction "
                         "1, 1/2, 1/4, 1/8 (attention, selection, scatter, Euler per kernel)")
+    p.add_argument("--proj", action="store_true",
+                   help="also time the fused QKV projection with the cache write "
+                        "(hsa_qkv_project) against library linear + hsa_kv_update")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 512 MiB device copy 3 times (reference for HBM counters)")
     return p.parse_args()
@@ -251,6 +254,60 @@ def run_loop(hs, synth, torch, cfg):
             "wall_s": wall}
 
 
+def run_proj(hs, torch, reps=10):
+    """Fused QKV projection of the active rows with the cache write in its epilogue
+    (hsa_qkv_project), against the unfused pair: torch's linear (hipBLASLt) into a [|A|, 3HD]
+    buffer, then hsa_kv_update of its K/V parts.  Seeded N(0,1) bf16 inputs on the device;
+    model dim = H * D; HIP events around each call (mean of reps after one warm-up)."""
+    dev = torch.device("cuda")
+    out = {"workload": "QKV projection of the active rows + cache write", "points": []}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for name, B, A, N, H, D in (("single step", 1, 16380, 32760, 12, 128),
+                                ("large-head sweep f=0.5", 1, 37800, 75600, 40, 128),
+                                ("aggressive pair, 10% active", 2, 7560, 75600, 40, 128)):
+        HD, Dm = H * D, H * D
+        gen = torch.Generator(device=dev).manual_seed(20260512)
+        x = torch.randn((B, A, Dm), device=dev, generator=gen).to(torch.bfloat16)
+        w = (torch.randn((3 * HD, Dm), device=dev, generator=gen) / Dm ** 0.5).to(torch.bfloat16)
+        bias = torch.zeros(3 * HD, device=dev, dtype=torch.bfloat16)
+        kc = torch.zeros((B, N, H, D), device=dev, dtype=torch.bfloat16)
+        vc = torch.zeros_like(kc)
+        idx = torch.from_numpy(np.sort(np.random.default_rng(0).choice(N, A, replace=False))
+                               .astype(np.int32)).to(dev)
+        q = torch.empty((B, A, H, D), device=dev, dtype=torch.bfloat16)
+        flops = 2.0 * B * A * Dm * 3 * HD
+
+        def unfused():
+            y = torch.nn.functional.linear(x, w, bias)
+            kn = y[..., HD:2 * HD].contiguous().view(B, A, H, D)
+            vn = y[..., 2 * HD:].contiguous().view(B, A, H, D)
+            hs.hsa_kv_update(kc, vc, kn, vn, idx, A)
+
+        t_f = timed(lambda: hs.hsa_qkv_project(x, w, bias, q, kc, vc, idx, A))
+        t_u = timed(unfused)
+        t_l = timed(lambda: torch.nn.functional.linear(x, w, bias))
+        out["points"].append({"shape": name, "batch": B, "n_active": A, "n_tokens": N,
+                              "model_dim": Dm, "out_dim": 3 * HD, "gflop": flops / 1e9,
+                              "fused_ms": t_f, "fused_tflops": flops / t_f / 1e9,
+                              "fused_frac_of_bf16_peak": flops / t_f / 1e9 / PEAK_BF16_TFLOPS,
+                              "unfused_ms": t_u, "library_linear_ms": t_l,
+                              "library_linear_tflops": flops / t_l / 1e9})
+        print(f"bench: projection {name}: fused {t_f:.3f} ms, unfused {t_u:.3f} ms", file=sys.stderr,
+              flush=True)
+    return out
+
+
 def run_sweep(hs, synth, torch, reps=5):
     """Large-head sweep (N=75600 on a 21x45x80 grid, 40 heads x 128, 64 channels): per active
     fraction f, each kernel of one iteration timed alone with HIP events (mean of reps).
@@ -377,6 +434,9 @@ def main():
     if args.pair:
         print("bench: aggressive pair loop", file=sys.stderr, flush=True)
         res["aggressive_pair"] = run_loop(hs, synth, torch, synth.aggressive_pair())
+    if args.proj:
+        print("bench: fused QKV projection", file=sys.stderr, flush=True)
+        res["qkv_projection"] = run_proj(hs, torch)
     if args.sweep:
         print("bench: large-head sweep", file=sys.stderr, flush=True)
         res["large_head_sweep"] = run_sweep(hs, synth, torch)

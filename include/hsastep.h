@@ -165,6 +165,33 @@ int hsa_attention_active(const uint16_t* q_active, const uint16_t* k_cache,
                          float softmax_scale, void* stream);
 
 /*
+ * Fused QKV projection of the active tokens with the cache write as its epilogue
+ * ([HSA-nl] §2.2 items 1-2: only the active tokens go through the model's projections,
+ * and their fresh K and V rows overwrite their cache slots).  With HD = heads*head_dim,
+ *   Y = x_active W^T (+ bias), fp32 accumulation, rounded to bf16 per element:
+ *   Y[b*n_active + a, 0:HD)      -> q_out[b, a]
+ *   Y[b*n_active + a, HD:2HD)    -> k_cache[b, active_idx[a]]
+ *   Y[b*n_active + a, 2HD:3HD)   -> v_cache[b, active_idx[a]]
+ * It replaces a projection into k_new/v_new followed by hsa_kv_update.
+ *
+ *   x_active           [batch, n_active, model_dim] bf16, active order (16-byte aligned)
+ *   w_qkv              [3*HD, model_dim] bf16: the Q, K and V weights stacked by output
+ *                      row (the usual [out_features, in_features] layout; 16-byte aligned)
+ *   bias_or_null       [3*HD] bf16, or NULL
+ *   q_out              [batch, n_active, heads, head_dim] bf16 output
+ *   k_cache, v_cache   [batch, n_tokens, heads, head_dim] bf16, in place: only the rows of
+ *                      the active slots are written
+ *   active_idx         [n_active] int32, slots in [0, n_tokens) (others are skipped)
+ * model_dim must be a positive multiple of 64 (else HSASTEP_ERR_UNSUPPORTED), and
+ * x_active and w_qkv each below 4 GiB.  n_active == 0 is a no-op.  Outputs must not
+ * alias inputs.
+ */
+int hsa_qkv_project(const uint16_t* x_active, const uint16_t* w_qkv, const uint16_t* bias_or_null,
+                    uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache,
+                    const int32_t* active_idx, int64_t n_active, int64_t n_tokens, int32_t batch,
+                    int32_t heads, int32_t head_dim, int32_t model_dim, void* stream);
+
+/*
  * Cached Euler update ([HSA-nl] §2.3), one branch-free pass over all N tokens:
  *   v_cache[n] <- v_fresh[active_pos[n]]     for active tokens (active_pos[n] >= 0)
  *   x[n]       <- x[n] + dt * v_cache[n]     for every token,

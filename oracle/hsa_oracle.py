@@ -196,6 +196,25 @@ def attention_active(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     return out
 
 
+def qkv_project(x_bits: np.ndarray, w_bits: np.ndarray, bias_bits, heads: int, head_dim: int):
+    """[HSA-nl §2.2, items 1-2]: only the active tokens go through the projections; their
+    fresh K and V rows are what the cache takes.
+
+    x [B, |A|, Dm], w [3*H*D, Dm] (Q, K, V weights stacked by output row), bias [3*H*D] or
+    None, all bf16 bits -> (q, k, v) float64 [B, |A|, H, D]: y = x w^T + bias, evaluated in
+    float64 from the bf16 values (no rounding).
+    """
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(w_bits)
+    y = x @ w.T
+    if bias_bits is not None:
+        y = y + bf16_bits_to_f64(bias_bits)
+    B, A = x.shape[0], x.shape[1]
+    hd = heads * head_dim
+    parts = [y[:, :, p * hd:(p + 1) * hd].reshape(B, A, heads, head_dim) for p in range(3)]
+    return parts[0], parts[1], parts[2]
+
+
 # ----------------------------------------------------------------------------- Euler
 
 

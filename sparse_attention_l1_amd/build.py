@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhsastep.so")
 
 SOURCES = ["abi.cpp", "host.cpp", "score.hip", "rank.hip", "active.hip", "rows.hip", "euler.hip",
-           "attn.hip"]
+           "attn.hip", "proj.hip"]
 
 ARCH = "gfx950"
 # files whose fp32 results are specified to the bit: no multiply-add contraction

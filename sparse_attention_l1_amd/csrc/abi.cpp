@@ -195,6 +195,34 @@ HSASTEP_API int hsa_attention_active(const uint16_t* q_active, const uint16_t* k
                     "attention");
 }
 
+HSASTEP_API int hsa_qkv_project(const uint16_t* x_active, const uint16_t* w_qkv,
+                                const uint16_t* bias_or_null, uint16_t* q_out, uint16_t* k_cache,
+                                uint16_t* v_cache, const int32_t* active_idx, int64_t n_active,
+                                int64_t n_tokens, int32_t batch, int32_t heads, int32_t head_dim,
+                                int32_t model_dim, void* stream) {
+  if (n_tokens < 1 || n_tokens > INT32_MAX || n_active < 0 || n_active > n_tokens ||
+      batch < 1 || heads < 1 || head_dim < 1)
+    return fail(HSASTEP_ERR_ARG, "need 1 <= n_tokens < 2^31, 0 <= n_active <= n_tokens, "
+                                 "batch, heads, head_dim >= 1");
+  if (model_dim < 64 || model_dim % 64 != 0)
+    return fail(HSASTEP_ERR_UNSUPPORTED, "model_dim must be a positive multiple of 64");
+  const int64_t hd = int64_t(heads) * head_dim;
+  const int64_t m_rows = int64_t(batch) * n_active;
+  if (3 * hd > INT32_MAX / 2 || m_rows > INT32_MAX || int64_t(batch) * n_tokens > INT32_MAX)
+    return fail(HSASTEP_ERR_UNSUPPORTED, "sizes too large");
+  if (m_rows * model_dim * 2 >= (int64_t(1) << 32) || 3 * hd * model_dim * 2 >= (int64_t(1) << 32))
+    return fail(HSASTEP_ERR_UNSUPPORTED, "x_active and w_qkv must each be below 4 GiB");
+  if (n_active == 0) return ok();
+  if (!x_active || !w_qkv || !q_out || !k_cache || !v_cache || !active_idx)
+    return fail(HSASTEP_ERR_ARG, "null pointer argument");
+  if (!aligned16(x_active) || !aligned16(w_qkv))
+    return fail(HSASTEP_ERR_ARG, "x_active / w_qkv must be 16-byte aligned");
+  return hip_status(hsastep::launch_qkv_project(x_active, w_qkv, bias_or_null, q_out, k_cache,
+                                                v_cache, active_idx, n_active, n_tokens, batch,
+                                                heads, head_dim, model_dim, as_stream(stream)),
+                    "qkv projection");
+}
+
 HSASTEP_API int hsa_euler_step(float* x, float* v_cache, const float* v_fresh,
                                const int32_t* active_pos, int64_t n_active, int64_t n_tokens,
                                int32_t channels, float sigma_cur, float sigma_next, void* stream) {

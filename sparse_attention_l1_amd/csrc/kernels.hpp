@@ -37,6 +37,13 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
                             uint16_t* out, int64_t n_active, int64_t n_tokens, int batch, int heads,
                             int head_dim, float softmax_scale, hipStream_t stream);
 
+// proj.hip: fused QKV projection of the active rows; Q compacted, K/V into their cache slots.
+hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w, const uint16_t* bias,
+                              uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache,
+                              const int32_t* active_idx, int64_t n_active, int64_t n_tokens,
+                              int batch, int heads, int head_dim, int model_dim,
+                              hipStream_t stream);
+
 // euler.hip: cached Euler update over all tokens.
 hipError_t launch_euler(float* x, float* v_cache, const float* v_fresh, const int32_t* active_pos,
                         int64_t n_active, int64_t n_tokens, int channels, float sigma_cur,

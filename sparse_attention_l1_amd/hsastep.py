@@ -36,6 +36,8 @@ _SIGS = {
     "hsa_kv_update": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p], ctypes.c_int),
     "hsa_attention_active": ([_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _f, _p], ctypes.c_int),
     "hsa_euler_step": ([_p, _p, _p, _p, _i64, _i64, _i32, _f, _f, _p], ctypes.c_int),
+    "hsa_qkv_project": ([_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p],
+                        ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -176,6 +178,28 @@ def hsa_attention_active(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                     _dev(v_cache, "v_cache", _BF16), _dev(out, "out", _BF16), A, N,
                                     B, H, D, float(softmax_scale), _stream(stream)),
            "hsa_attention_active")
+
+
+def hsa_qkv_project(x_active: torch.Tensor, w_qkv: torch.Tensor, bias: Optional[torch.Tensor],
+                    q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    active_idx: torch.Tensor, n_active: int, stream=None) -> None:
+    """x_active [B, >= n_active, Dm] bf16 (rows past n_active unused), w_qkv [3*H*D, Dm],
+    bias [3*H*D] or None, q_out [B, >= n_active, H, D], caches [B, N, H, D]."""
+    B, N, H, D = k_cache.shape
+    dm = x_active.shape[-1]
+    if v_cache.shape != k_cache.shape or w_qkv.shape != (3 * H * D, dm) or \
+            x_active.shape[0] != B or q_out.shape[0] != B or q_out.shape[2:] != (H, D) or \
+            (bias is not None and bias.shape != (3 * H * D,)):
+        raise ValueError("shape mismatch")
+    if x_active.shape[1] != n_active or q_out.shape[1] != n_active:
+        if B != 1:
+            raise ValueError("with batch > 1, x_active and q_out must hold exactly n_active rows")
+    _check(lib.hsa_qkv_project(
+        _dev(x_active, "x_active", _BF16), _dev(w_qkv, "w_qkv", _BF16),
+        None if bias is None else _dev(bias, "bias", _BF16), _dev(q_out, "q_out", _BF16),
+        _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(active_idx, "active_idx", (torch.int32,)), n_active, N, B, H, D, dm,
+        _stream(stream)), "hsa_qkv_project")
 
 
 def hsa_euler_step(x: torch.Tensor, v_cache: torch.Tensor, v_fresh: torch.Tensor,

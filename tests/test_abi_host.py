@@ -128,6 +128,18 @@ def test_kv_attention_euler_gather_reject(hs):
     assert ga(None, None, None, 0, 8, 8, None) == hs.OK
 
 
+def test_qkv_project_rejects(hs):
+    f = lambda *a: call(hs, "hsa_qkv_project", *a)
+    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 64, 96, None) == hs.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 9, 8, 1, 2, 64, 64, None) == hs.ERR_ARG
+    assert f(None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 64, 64, None) == hs.ERR_ARG
+    assert f(ctypes.c_void_p((1 << 20) + 2), FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 64,
+             64, None) == hs.ERR_ARG
+    assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, 1 << 21, 1, 16, 128, 4096,
+             None) == hs.ERR_UNSUPPORTED                            # x_active above 4 GiB
+    assert f(None, None, None, None, None, None, None, 0, 8, 1, 2, 64, 64, None) == hs.OK
+
+
 def test_n_active_closed_form_matches_oracle(hs):
     r = np.random.default_rng(11)
     for T in (1, 4, 8, 12, 40):
