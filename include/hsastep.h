@@ -9,6 +9,8 @@
  *   hsa_kv_update         fresh K/V rows of the active tokens into the per-layer cache
  *   hsa_attention_active  the active queries against all N cached keys/values
  *   hsa_euler_step        cached Euler update of all N latents
+ * and, fusing the model's projection with the cache write:
+ *   hsa_qkv_project       Q/K/V of the active rows; K/V straight into their cache slots
  *
  * Pages that define the operations (cited below by short name):
  *   [HSA-nl] "Technische Samenvatting: Heterogene Staptoewijzing (HSA) voor
