@@ -212,6 +212,8 @@ HSASTEP_API int hsa_qkv_project(const uint16_t* x_active, const uint16_t* w_qkv,
     return fail(HSASTEP_ERR_UNSUPPORTED, "sizes too large");
   if (m_rows * model_dim * 2 >= (int64_t(1) << 32) || 3 * hd * model_dim * 2 >= (int64_t(1) << 32))
     return fail(HSASTEP_ERR_UNSUPPORTED, "x_active and w_qkv must each be below 4 GiB");
+  if (((m_rows + 255) / 256) * ((3 * hd + 255) / 256) > INT32_MAX)
+    return fail(HSASTEP_ERR_UNSUPPORTED, "grid too large");
   if (n_active == 0) return ok();
   if (!x_active || !w_qkv || !q_out || !k_cache || !v_cache || !active_idx)
     return fail(HSASTEP_ERR_ARG, "null pointer argument");
