@@ -39,7 +39,6 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 constexpr int kWaitVm0 = 0x0F70;   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt unconstrained)
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 
-
 struct ProjArgs {
   const uint16_t* x;
   const uint16_t* w;
