@@ -9,7 +9,9 @@
 //   x[n] = fl(x[n] + fl(dt * v))                          (no fused multiply-add)
 //
 // HBM bound: reads x, one velocity row and active_pos, writes x and the fresh
-// rows into the cache.  One thread handles 4 channels (16-byte accesses).
+// rows into the cache.  A thread handles kItems 16-byte pieces (4 channels each) and
+// issues all their loads before using any, so enough bytes are in flight to cover the
+// HBM latency of the dependent load (active_pos, then the velocity row).
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -17,30 +19,53 @@
 namespace hsastep {
 namespace {
 
+constexpr int kItems = 4;   // 16-byte pieces per thread, all loads issued before any use
+
+// Idx: 32-bit piece indices when the latent has fewer than 2^31 pieces (cheap division)
+template <typename Idx>
 __global__ __launch_bounds__(256) void euler_vec4_kernel(float4* __restrict__ x,
                                                          float4* __restrict__ v_cache,
                                                          const float4* __restrict__ v_fresh,
                                                          const int32_t* __restrict__ active_pos,
-                                                         int64_t n_active, int64_t n_tokens,
-                                                         int vecs_per_row, float dt) {
+                                                         int64_t n_active, Idx total,
+                                                         Idx vecs_per_row, float dt) {
 #pragma clang fp contract(off)
-  const int64_t total = n_tokens * vecs_per_row;
-  for (int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
-       t += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t n = t / vecs_per_row;
-    const int64_t c = t - n * vecs_per_row;
-    const int32_t pos = active_pos[n];
-    const bool act = pos >= 0 && pos < n_active;
-    const float4* src = act ? v_fresh + int64_t(pos) * vecs_per_row + c : v_cache + t;
-    const float4 v = *src;
-    float4 xv = x[t];
-    if (act) v_cache[t] = v;
-    // contraction is off in this scope (and for the file): product, then sum
-    xv.x = xv.x + dt * v.x;
-    xv.y = xv.y + dt * v.y;
-    xv.z = xv.z + dt * v.z;
-    xv.w = xv.w + dt * v.w;
-    x[t] = xv;
+  const Idx span = Idx(blockDim.x) * kItems;
+  for (Idx base = Idx(blockIdx.x) * span + threadIdx.x; base < total;
+       base += Idx(gridDim.x) * span) {
+    // piece k of this thread is base + k * blockDim.x: consecutive threads stay on
+    // consecutive 16-byte pieces, and every load of the group is in flight together
+    int32_t pos[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const Idx t = base + Idx(k) * blockDim.x;
+      pos[k] = t < total ? active_pos[t / vecs_per_row] : -1;
+    }
+    float4 v[kItems], xv[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const Idx t = base + Idx(k) * blockDim.x;
+      if (t < total) {
+        const Idx c = t % vecs_per_row;
+        const bool act = pos[k] >= 0 && pos[k] < n_active;
+        const float4* src = act ? v_fresh + int64_t(pos[k]) * vecs_per_row + c : v_cache + t;
+        v[k] = *src;
+        xv[k] = x[t];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const Idx t = base + Idx(k) * blockDim.x;
+      if (t < total) {
+        if (pos[k] >= 0 && pos[k] < n_active) v_cache[t] = v[k];
+        // contraction is off in this scope (and for the file): product, then sum
+        xv[k].x = xv[k].x + dt * v[k].x;
+        xv[k].y = xv[k].y + dt * v[k].y;
+        xv[k].z = xv[k].z + dt * v[k].z;
+        xv[k].w = xv[k].w + dt * v[k].w;
+        x[t] = xv[k];
+      }
+    }
   }
 }
 
@@ -73,13 +98,19 @@ hipError_t launch_euler(float* x, float* v_cache, const float* v_fresh, const in
   const float dt = sigma_next - sigma_cur;   // one fp32 rounding
   const bool vec = channels % 4 == 0;
   const int64_t work = n_tokens * (vec ? channels / 4 : channels);
-  int64_t blocks = (work + 255) / 256;
+  const int64_t per_block = vec ? 256 * kItems : 256;
+  int64_t blocks = (work + per_block - 1) / per_block;
   if (blocks > 65536) blocks = 65536;
-  if (vec)
-    euler_vec4_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(
+  if (vec && work + 256 * kItems < (int64_t(1) << 31))
+    euler_vec4_kernel<uint32_t><<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(
         reinterpret_cast<float4*>(x), reinterpret_cast<float4*>(v_cache),
-        reinterpret_cast<const float4*>(v_fresh), active_pos, n_active, n_tokens, channels / 4,
-        dt);
+        reinterpret_cast<const float4*>(v_fresh), active_pos, n_active, uint32_t(work),
+        uint32_t(channels / 4), dt);
+  else if (vec)
+    euler_vec4_kernel<uint64_t><<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(
+        reinterpret_cast<float4*>(x), reinterpret_cast<float4*>(v_cache),
+        reinterpret_cast<const float4*>(v_fresh), active_pos, n_active, uint64_t(work),
+        uint64_t(channels / 4), dt);
   else
     euler_scalar_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, stream>>>(
         x, v_cache, v_fresh, active_pos, n_active, n_tokens, channels, dt);
