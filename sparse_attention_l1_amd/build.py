@@ -20,13 +20,13 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhsastep.so")
 
 SOURCES = ["abi.cpp", "host.cpp", "score.hip", "rank.hip", "active.hip", "rows.hip", "euler.hip",
-           "attn.hip", "proj.hip"]
+           "attn.hip", "attn_pipe.hip", "proj.hip"]
 
 ARCH = "gfx950"
 # files whose fp32 results are specified to the bit: no multiply-add contraction
 EXACT = ("score.hip", "euler.hip")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
-          f"-I{INCLUDE}", f"-I{CSRC}"]
+          f"-I{INCLUDE}", f"-I{CSRC}", f"-I{BUILD}"]
 # device code: gfx950 only; no packed-fp32 instructions (v_pk_{add,mul,fma}_f32)
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -53,9 +53,20 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def generate_sources() -> None:
+    """Writes the generated attention key loop (attn_loop.inc) into the build folder."""
+    sys.path.insert(0, CSRC)
+    try:
+        import attn_loop_gen
+    finally:
+        sys.path.pop(0)
+    attn_loop_gen.write(os.path.join(BUILD, "attn_loop.inc"))
+
+
 def build(verbose: bool = False) -> str:
     """Compiles every source and links the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    generate_sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"

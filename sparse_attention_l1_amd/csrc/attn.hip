@@ -379,6 +379,9 @@ hipError_t launch_cfg(const uint16_t* q, const uint16_t* k, const uint16_t* v, u
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                             uint16_t* out, int64_t n_active, int64_t n_tokens, int batch, int heads,
                             int head_dim, float softmax_scale, hipStream_t stream) {
+  if (attention_pipe_fits(n_tokens, heads, head_dim))
+    return launch_attention_pipe(q, k_cache, v_cache, out, n_active, n_tokens, batch, heads,
+                                 softmax_scale, stream);
   if (head_dim == 128)
     return launch_cfg<128, 1, 8, 128, 2>(q, k_cache, v_cache, out, n_active, n_tokens, batch, heads,
                                       softmax_scale, stream);

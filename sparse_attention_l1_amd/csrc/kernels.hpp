@@ -37,6 +37,14 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const ui
                             uint16_t* out, int64_t n_active, int64_t n_tokens, int batch, int heads,
                             int head_dim, float softmax_scale, hipStream_t stream);
 
+// attn_pipe.hip: the head_dim 128 path of launch_attention (one wavefront per SIMD, 64
+// queries each, hand-scheduled key loop); fits() says whether a shape can take it.
+bool attention_pipe_fits(int64_t n_tokens, int heads, int head_dim);
+hipError_t launch_attention_pipe(const uint16_t* q, const uint16_t* k_cache,
+                                 const uint16_t* v_cache, uint16_t* out, int64_t n_active,
+                                 int64_t n_tokens, int batch, int heads, float softmax_scale,
+                                 hipStream_t stream);
+
 // proj.hip: fused QKV projection of the active rows; Q compacted, K/V into their cache slots.
 hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w, const uint16_t* bias,
                               uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache,

@@ -170,6 +170,17 @@ ATTN_CASES = [
     (1, 200, 700, 2, 128, 8.0),     # peaky softmax
     (1, 200, 700, 2, 64, 16.0),     # very peaky
     (2, 40, 3000, 5, 128, 1.0),
+    # head_dim 128 with N >= 256 takes the hand-scheduled kernel (attn_pipe.hip); N = 251 the
+    # other one.  N = 32 nb - 5 for nb = 9..16 ends the key loop at each of its 8 unrolled
+    # steps, with a ragged last block; N = 257 leaves one key in the last block.
+    (1, 70, 251, 1, 128, 1.0),
+    (1, 70, 256, 1, 128, 1.0),
+    (1, 70, 257, 2, 128, 1.0),
+] + [(1, 70, 32 * nb - 5, 1, 128, 1.0) for nb in range(9, 17)] + [
+    (1, 1, 600, 1, 128, 1.0),       # one query: one wavefront with work, three without
+    (1, 257, 1000, 1, 128, 1.0),    # a second query tile holding one query
+    (1, 100, 900, 2, 128, 16.0),    # very peaky
+    (1, 64, 2000, 40, 128, 1.0),    # 40 heads (token stride 10 KB)
 ]
 
 
