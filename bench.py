@@ -35,7 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_single_step_pmc.txt")
-ATTN_SRC = os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", "attn.hip")
+# sources of the attention kernels: the counters summary is valid only for these exact files
+ATTN_SRCS = [os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", f)
+             for f in ("attn.hip", "attn_pipe.hip", "attn_loop_gen.py")]
 
 
 def parse():
@@ -77,7 +79,10 @@ def copy_calibration(torch):
 
 
 def attn_source_hash() -> str:
-    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ATTN_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():
