@@ -54,13 +54,16 @@ def _compile(src: str, verbose: bool) -> str:
 
 
 def generate_sources() -> None:
-    """Writes the generated attention key loop (attn_loop.inc) into the build folder."""
+    """Writes the generated assembly loops into the build folder: the attention key loop
+    (attn_loop.inc) and the projection's reduction loop (proj_loop.inc)."""
     sys.path.insert(0, CSRC)
     try:
         import attn_loop_gen
+        import proj_loop_gen
     finally:
         sys.path.pop(0)
     attn_loop_gen.write(os.path.join(BUILD, "attn_loop.inc"))
+    proj_loop_gen.write(os.path.join(BUILD, "proj_loop.inc"))
 
 
 def build(verbose: bool = False) -> str:

@@ -1,8 +1,8 @@
-"""Static checks of the generated attention key loop (test helper, no GPU).
+"""Static checks of the generated assembly loops: the attention key loop and the projection's
+reduction loop (test helper, no GPU).
 
-The loop is straight-line gfx950 assembly inside one inline-asm statement, so neither the
-compiler's hazard recognizer nor its waitcnt insertion sees it.  This module re-checks what
-they would have:
+Each loop is gfx950 assembly inside one inline-asm statement, so neither the compiler's hazard
+recognizer nor its waitcnt insertion sees it.  This module re-checks what they would have:
 
   - wait states (each instruction one, s_nop N = N + 1):
       MFMA result  -> any non-MFMA access       >= 12
@@ -14,7 +14,10 @@ they would have:
   - LDS results are used only after an lgkmcnt wait retires them, no register with an LDS
     result in flight is written, and at most 15 LDS operations are in flight;
   - every register the body touches is one of its operands or clobbers;
-  - LDS offsets stay inside the 128 KB the kernel allocates.
+  - LDS offsets stay inside the 128 KB the kernel allocates;
+  - (projection) a scalar walk of the loop's control flow: every stage of the reduction is
+    loaded once, complete, into the buffer it is read from, with the barriers that order the
+    four wavefronts' loads and reads.
 """
 from __future__ import annotations
 
@@ -29,13 +32,14 @@ MFMA_WS = 12
 LDS_BYTES = 131072
 
 
-def load_generator():
+def load_generator(name="attn_loop_gen"):
     sys.path.insert(0, CSRC)
     try:
-        import attn_loop_gen
+        import importlib
+        mod = importlib.import_module(name)
     finally:
         sys.path.pop(0)
-    return attn_loop_gen
+    return mod
 
 
 def regs(tok):
@@ -251,3 +255,134 @@ def check_lds_bounds(gen):
         if m0 and int(m0.group(1)) + 3 * 1024 + 1024 > LDS_BYTES:
             errors.append(line)
     return errors
+
+
+# ------------------------------------------------------------------ the projection's loop
+
+def proj_traces(gen, max_stages=5):
+    """(name, instruction list): the prologue, n stages with the loop's exit test, the exit."""
+    body = gen.generate()
+    pro = body[:body.index(".Lploop:")]
+    done = body[body.index(".Lpdone:") + 1:]
+    tail = [f"s_add_u32 s{gen.STAGE}, s{gen.STAGE}, 1", f"s_cmp_eq_u32 s{gen.STAGE}, s{gen.NSTAGE}",
+            "s_cbranch_scc1 .Lpdone"]
+    for n in range(1, max_stages + 1):
+        t = list(pro)
+        for k in range(n):
+            t += gen.stage(k % 2) + tail
+        yield f"stages={n}", t + done
+
+
+def check_proj_hazards(gen):
+    errors = []
+    for name, t in proj_traces(gen):
+        c = Checker(name)
+        c.run(t)
+        errors += c.errors
+    return errors
+
+
+def check_proj_lds_bounds(gen, lds_bytes=LDS_BYTES):
+    """Fragment reads: row R < 256 of a 128-byte-row region, any chunk, plus the immediate
+    offset (the W addresses carry the W region base); tile loads: m0 immediate plus the
+    wavefront's 1 KB slot row."""
+    errors = []
+    row_end = max(r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 16 for r in range(256) for c in range(8))
+    for line in gen.generate():
+        m = re.search(r"offset:(\d+)", line)
+        if line.startswith("ds_read_b128") and m:
+            addr = int(re.search(r"v(\d+) offset", line).group(1))
+            base = gen.WBUF[0] if gen.WADDR <= addr < gen.WADDR + 16 else 0
+            if base + row_end + int(m.group(1)) > lds_bytes:
+                errors.append(line)
+        m0 = re.match(r"s_add_u32 m0, s\d+, (\d+)", line)
+        if m0 and int(m0.group(1)) + 3 * 1024 + 1024 > lds_bytes:
+            errors.append(line)
+    return errors
+
+
+def proj_stage_walk(gen, nstage, max_instructions=200000):
+    """Runs the generated loop's control flow for one wavefront with nstage stages, modelling
+    the scalar registers it uses (stage counter, descriptor offset and range), the tile loads
+    (which stage and which buffer part each fetches), vmcnt waits, barriers and fragment
+    reads.  Returns (stages read per k-step, list of errors)."""
+    body = [l for l in gen.generate() if not l.startswith(";")]
+    labels = {l[:-1]: i for i, l in enumerate(body) if l.endswith(":")}
+    sreg = {gen.NSTAGE: nstage}
+    desc_off = {gen.XDESC: 0, gen.WDESC: 0}
+    desc_live = {gen.XDESC: True, gen.WDESC: True}
+    scc, m0, pc, steps = False, None, 0, 0
+    inflight, content, errors, reads = [], {}, [], []
+    last_read = {}          # buffer -> instruction count of the latest read
+    barriers = []           # instruction counts of barriers
+    landed = {}             # buffer -> instruction count of the wait that completed its last load
+    stage_loads = {}
+    val = lambda t: sreg.get(int(t[1:]), 0) if t.startswith("s") else int(t)
+    while pc < len(body):
+        steps += 1
+        if steps > max_instructions:
+            errors.append("no exit")
+            break
+        line = body[pc]
+        pc += 1
+        if line.endswith(":"):
+            continue
+        op, ops = parse(line)
+        if op == "s_mov_b32" and ops[0] != "m0" and ops[1] != "m0":
+            sreg[int(ops[0][1:])] = val(ops[1])
+        elif op == "s_add_u32" and ops[0] == "m0":
+            m0 = int(ops[2])
+        elif op == "s_add_u32":
+            d = int(ops[0][1:])
+            if d in desc_off:
+                desc_off[d] += val(ops[2])
+            else:
+                sreg[d] = val(ops[1]) + val(ops[2])
+        elif op in ("s_cmp_ge_u32", "s_cmp_eq_u32"):
+            x, y = val(ops[0]), val(ops[1])
+            scc = x >= y if op == "s_cmp_ge_u32" else x == y
+        elif op == "s_cselect_b32":
+            d = int(ops[0][1:]) - 2
+            if scc and d in desc_live:
+                desc_live[d] = False
+        elif op == "s_cbranch_scc1":
+            if scc:
+                pc = labels[ops[0]]
+        elif op == "s_branch":
+            pc = labels[ops[0]]
+        elif op == "s_barrier":
+            barriers.append(steps)
+        elif op == "buffer_load_dwordx4":
+            d = int(re.match(r"s\[(\d+):", ops[1]).group(1))
+            buf = (m0 % gen.WBUF[0]) // (gen.XBUF[1] - gen.XBUF[0])
+            part = ("X" if d == gen.XDESC else "W", (m0 % (gen.XBUF[1] - gen.XBUF[0])) // gen.LOAD_BYTES)
+            st = desc_off[d] // 128 if desc_live[d] else None
+            if buf in last_read and not any(last_read[buf] < b for b in barriers):
+                errors.append(f"load into buffer {buf} with no barrier after its last read")
+            inflight.append((buf, part, st))
+            if st is not None:
+                stage_loads.setdefault(st, []).append((buf, part))
+        elif op == "s_waitcnt":
+            m = re.search(r"vmcnt\((\d+)\)", line)
+            if m:
+                while len(inflight) > int(m.group(1)):
+                    buf, part, st = inflight.pop(0)
+                    content.setdefault(buf, {})[part] = st
+                    landed[buf] = steps
+        elif op == "ds_read_b128":
+            buf = int(re.search(r"offset:(\d+)", line).group(1)) // (gen.XBUF[1] - gen.XBUF[0])
+            if any(b == buf for b, _, _ in inflight):
+                errors.append(f"read of buffer {buf} while this wavefront still loads into it")
+            got = set(content.get(buf, {}).values())
+            if len(content.get(buf, {})) != 16 or len(got) != 1:
+                errors.append(f"read of incomplete buffer {buf}: {content.get(buf)}")
+            elif buf in landed and not any(landed[buf] < b for b in barriers):
+                errors.append(f"read of buffer {buf} with no barrier after its loads landed")
+            last_read[buf] = steps
+            reads.append(got.pop() if len(got) == 1 else "?")
+    if sreg.get(gen.STAGE) != nstage:
+        errors.append(f"loop ended after {sreg.get(gen.STAGE)} stages, not {nstage}")
+    for st in range(nstage):
+        if sorted(stage_loads.get(st, [])) != sorted((st % 2, (t, i)) for t in "XW" for i in range(8)):
+            errors.append(f"stage {st} loaded as {stage_loads.get(st)}")
+    return [reads[i] for i in range(0, len(reads), 8)], errors

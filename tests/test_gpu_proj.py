@@ -35,7 +35,15 @@ def close(got_bits, want, bound, label):
     assert np.all(err <= lim), label
 
 
-def run_case(hs, B, A, N, H, D, Dm, with_bias, seed, bad_slot=False, sample=None):
+def offset_copy(t):
+    """The same values at a device address 2 bytes past an 8-byte boundary."""
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    out = flat[1:].view(t.shape)
+    out.copy_(t)
+    return out
+
+
+def run_case(hs, B, A, N, H, D, Dm, with_bias, seed, bad_slot=False, sample=None, misalign=False):
     r = np.random.default_rng(seed)
     HD = H * D
     x = bits(r.standard_normal((B, A, Dm)) * 0.5)
@@ -48,6 +56,9 @@ def run_case(hs, B, A, N, H, D, Dm, with_bias, seed, bad_slot=False, sample=None
     vc0 = bits(r.standard_normal((B, N, H, D)))
     kd, vd = bits_dev(kc0), bits_dev(vc0)
     q = torch.full((B, A, H, D), 0x7F7F, dtype=torch.int16, device="cuda")
+    if misalign:
+        kd, vd, q = offset_copy(kd), offset_copy(vd), offset_copy(q)
+        assert q.data_ptr() % 8 == 2
     hs.hsa_qkv_project(bits_dev(x), bits_dev(w), None if bias is None else bits_dev(bias), q, kd,
                        vd, dev(idx), A)
     torch.cuda.synchronize()
@@ -72,9 +83,17 @@ def run_case(hs, B, A, N, H, D, Dm, with_bias, seed, bad_slot=False, sample=None
     (2, 300, 500, 3, 64, 128, True),      # ragged row and column tiles, batch 2, bias
     (1, 1000, 2000, 12, 128, 1536, False),
     (1, 257, 300, 1, 64, 320, True),      # 3*H*D = 192 < one column tile
+    (1, 513, 1000, 2, 64, 192, False),    # three stages of the reduction (odd count)
+    (1, 300, 700, 3, 30, 128, True),      # H*D = 90: columns of a 4-group straddle q/k/v
+    (2, 100, 400, 1, 6, 64, True),        # H*D = 6, one stage
 ])
 def test_qkv_project(hs, B, A, N, H, D, Dm, with_bias):
     run_case(hs, B, A, N, H, D, Dm, with_bias, seed=A + N + Dm)
+
+
+def test_qkv_project_unaligned_destinations(hs):
+    """q_out and the caches 2 bytes off an 8-byte boundary: per-value stores."""
+    run_case(hs, 2, 300, 500, 3, 64, 128, True, seed=17, misalign=True)
 
 
 def test_qkv_project_skips_invalid_slot(hs):
