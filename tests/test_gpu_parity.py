@@ -209,6 +209,31 @@ def test_attention(hs, B, A, N, H, D, qs):
     assert np.array_equal(host_bits(o3), host_bits(o)[:, sub])
 
 
+@pytest.mark.parametrize("N,D,late", [(2000, 128, (1500,)), (2000, 128, (1500, 1999)),
+                                       (700, 64, (650,))])
+def test_attention_late_outlier_key(hs, N, D, late):
+    """Keys far above every earlier score: 2^(s c - m) against the earlier reference max
+    would overflow fp32 (s c - m is about 400 in log2 units), so the kernels must move the
+    reference before using these keys; the output is the mean of the outliers' values."""
+    B, A, H = 1, 100, 2
+    r = np.random.default_rng(N + D)
+    qf = r.standard_normal((B, A, H, D)).astype(np.float32)
+    kf = r.standard_normal((B, N, H, D)).astype(np.float32)
+    qf[..., 0] = 40.0
+    kf[..., 0] = 0.0
+    for j in late:
+        kf[:, j, :, 0] = 80.0
+    q, k = synth.f32_to_bf16_bits(qf), synth.f32_to_bf16_bits(kf)
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, N, H, D)).astype(np.float32))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    want = oracle.attention_active(q, k, v, scale)
+    o = torch.empty((B, A, H, D), dtype=torch.int16, device="cuda")
+    hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
+    torch.cuda.synchronize()
+    attn_close(host_bits(o), want, f"outlier N{N} D{D} {late}")
+    assert not np.isnan(bf16_to_f64(host_bits(o))).any()
+
+
 def test_attention_zero_query_is_mean(hs):
     B, A, N, H, D = 1, 5, 999, 2, 128
     r = np.random.default_rng(1)
