@@ -28,8 +28,8 @@
 //   - Softmax in base 2 with scale*log2(e) folded into one FMA, per 32-key
 //     block.  Steady state needs no max: p = 2^(s*c - m) against a reference max
 //     m, row sums by bf16 dot products of the rounded p (the values the MFMA
-//     uses).  Only when a lane's block sum leaves (0, 2^8] (the first block, a
-//     new max far above m, or overflow) does the pair of lanes take the true max,
+//     uses).  Only when a lane's block sum exceeds 2^8 or is not a number (the first
+//     block, a new max far above m, or overflow) does the pair of lanes take the true max,
 //     rescale O and recompute the block.  The decision is per query, so a query's
 //     result never depends on its tile neighbours.
 //   - Workgroup order is XCD aware: consecutive workgroup ids go to different

@@ -4,7 +4,7 @@ Active-query full-context attention ("Technische Samenvatting: Heterogene Stapto
 voor Efficiënte Videogeneratie", §2.2 items 3-4): the active queries of one (b, h) attend to all
 N cached keys, O = softmax(Q_A K^T * scale) V.  The method is the one of attn.hip's kernel
 (transposed MFMAs, base-2 online softmax against a reference max, a rare path that takes the
-true max when a block's sum leaves (0, 2^8]); only the row sums differ (below).  This file
+true max when a block's sum exceeds 2^8 or is not a number); only the row sums differ (below).  This file
 fixes the order in which one wavefront issues the work, which the compiler does not find.
 
 Why hand scheduled.  One wavefront per SIMD owns 64 queries (two 32-query blocks qb = 0, 1),
