@@ -100,6 +100,12 @@ def test_qkv_project_skips_invalid_slot(hs):
     run_case(hs, 1, 64, 100, 2, 64, 64, True, seed=9, bad_slot=True)
 
 
+def test_qkv_project_unaligned_many_tiles(hs):
+    """More tiles than workgroups (each walks several) on the per-value store path."""
+    rows = synth.sample_rows(1, 9000, 48, tag=5)
+    run_case(hs, 1, 9000, 12000, 8, 96, 1024, True, seed=21, sample=rows, misalign=True)
+
+
 def test_qkv_project_full_size_single_step(hs):
     """16380 active rows of a 32760-token cache, 12 x 128 heads, model dim 1536: every stale
     row checked bit for bit, 64 sampled rows against the oracle."""
