@@ -19,6 +19,8 @@
 namespace hsastep {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int P, bool kVec4>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ v_prev,
                                                     const float* __restrict__ v_cur,
@@ -39,8 +41,9 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ v_
   if (kVec4) {
     // channels % 4 == 0 here: c0 < channels or the whole lane is padding
     if (c0 < channels) {
-      const float4 a = *reinterpret_cast<const float4*>(v_prev + row + c0);
-      const float4 b = *reinterpret_cast<const float4*>(v_cur + row + c0);
+      // read once per call: nontemporal loads stream the rows through the caches
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v_prev + row + c0));
+      const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v_cur + row + c0));
       p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w;
       c[0] = b.x; c[1] = b.y; c[2] = b.z; c[3] = b.w;
     } else {
