@@ -74,7 +74,7 @@ SELECT_CASES = [
     ("heavy", 75600, 64, (7560, 22680, 45360)),
     ("lognormal", 32760, 64, (16380, 16380)),
     ("ties", 20000, 4, (3000, 9000, 8000)),
-    # more than 512 chunks of 2048 tokens: workgroups then hold 4096 tokens each
+    # more than 512 chunks of 512 tokens: workgroups then hold 2560 tokens each
     ("levels", 1100000, 1, (100000, 350000, 0, 650000)),
     ("lognormal", 4097, 255, tuple([256] * 15 + [257])),
     ("lognormal", 333, 1, (100, 233)),
