@@ -192,20 +192,38 @@ def softmax_full(par, qb):
     return softmax_part(par, qb, 0, 4) + softmax_part(par, qb, 4, 8)
 
 
+# Calls of the rare-path and mask routines sit out of line, in stubs after the routines: the
+# common case falls through a branch that is not taken (a taken branch refetches instructions,
+# and with one wavefront per SIMD nothing else issues meanwhile).  The stub calls the routine
+# and branches back to the label after the call site.
+CALL_STUBS = {}            # call-site label -> the routine's address register pair
+
+
+def call_site(branch, routine_regs, label):
+    CALL_STUBS[label] = routine_regs
+    return [f"{branch} {label}_call", f"{label}:"]
+
+
+def call_stubs(body):
+    out = []
+    for l in body:
+        if l.endswith("_call") and l.startswith("s_cbranch"):
+            label = l.split()[1][:-len("_call")]
+            out += [f"{label}_call:", f"s_swappc_b64 {s(RET, 2)}, {CALL_STUBS[label]}",
+                    f"s_branch {label}"]
+    return out
+
+
 def check_and_fix(par, qb, label):
     """Calls the rare path if any lane's block sum is not in (-inf, 256]; then L += LS."""
-    return [f"v_cmp_nge_f32 vcc, 0x43800000, {v(LS + qb)}",
-            f"s_cbranch_vccz {label}",
-            f"s_swappc_b64 {s(RET, 2)}, {s(FIXA + 2 * (par * 2 + qb), 2)}",
-            f"{label}:",
-            f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(LS + qb)}"]
+    return ([f"v_cmp_nge_f32 vcc, 0x43800000, {v(LS + qb)}"] +
+            call_site("s_cbranch_vccnz", s(FIXA + 2 * (par * 2 + qb), 2), label) +
+            [f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(LS + qb)}"])
 
 
 def mask_call(par, qb, stepreg, label):
-    return [f"s_cmp_eq_u32 {s(STEP)}, {s(stepreg)}",
-            f"s_cbranch_scc0 {label}",
-            f"s_swappc_b64 {s(RET, 2)}, {s(MASKA + 2 * (par * 2 + qb), 2)}",
-            f"{label}:"]
+    return ([f"s_cmp_eq_u32 {s(STEP)}, {s(stepreg)}"] +
+            call_site("s_cbranch_scc1", s(MASKA + 2 * (par * 2 + qb), 2), label))
 
 
 def cost(op):
@@ -468,6 +486,7 @@ def generate():
         for qb in range(2):
             body.extend(fix_routine(par, qb))
             body.extend(mask_routine(par, qb))
+    body.extend(call_stubs(body))
     body += [".Ldone:",
              "s_waitcnt vmcnt(0) lgkmcnt(0)",
              f"s_mov_b32 m0, {s(M0SAVE)}",

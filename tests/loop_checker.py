@@ -166,20 +166,34 @@ def routine(body, label):
     raise ValueError(label)
 
 
+def _call(gen, body, line):
+    """The s_swappc line and the called routine."""
+    p = parse(line)
+    addr = int(re.search(r"s\[(\d+):", p[1][1]).group(1))
+    if gen.FIXA <= addr < gen.FIXA + 8:
+        k = (addr - gen.FIXA) // 2
+        return [line] + routine(body, f".Lfix{k // 2}{k % 2}")
+    k = (addr - gen.MASKA) // 2
+    return [line] + routine(body, f".Lmask{k // 2}{k % 2}")
+
+
 def expand(gen, lines, body, take_calls):
-    """Inlines the called routine after every s_swappc when take_calls (the taken path)."""
+    """With take_calls (the taken path), follows every branch to an out-of-line call stub: the
+    stub's call, the called routine, and the stub's branch back."""
     out = []
     for l in lines:
         out.append(l)
         p = parse(l)
-        if take_calls and p and p[0] == "s_swappc_b64":
-            addr = int(re.search(r"s\[(\d+):", p[1][1]).group(1))
-            if gen.FIXA <= addr < gen.FIXA + 8:
-                k = (addr - gen.FIXA) // 2
-                out.extend(routine(body, f".Lfix{k // 2}{k % 2}"))
-            else:
-                k = (addr - gen.MASKA) // 2
-                out.extend(routine(body, f".Lmask{k // 2}{k % 2}"))
+        if take_calls and p and p[0] in ("s_cbranch_vccnz", "s_cbranch_scc1") and \
+                p[1][0].endswith("_call"):
+            stub = body.index(p[1][0] + ":")
+            call, back = body[stub + 1], body[stub + 2]
+            assert call.startswith("s_swappc_b64") and back == "s_branch " + p[1][0][:-5], \
+                f"malformed call stub {p[1][0]}"
+            out.extend(_call(gen, body, call))
+            out.append(back)
+        elif take_calls and p and p[0] == "s_swappc_b64":
+            out.extend(_call(gen, body, l)[1:])
     return out
 
 
