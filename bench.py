@@ -35,9 +35,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_single_step_pmc.txt")
-# sources of the attention kernels: the counters summary is valid only for these exact files
+# sources of the attention kernels: the counters summary is valid only for this exact code
+# (the two HIP files and the key loop the generator emits; not the generator's comments)
 ATTN_SRCS = [os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", f)
-             for f in ("attn.hip", "attn_pipe.hip", "attn_loop_gen.py")]
+             for f in ("attn.hip", "attn_pipe.hip")]
 
 
 def parse():
@@ -79,9 +80,16 @@ def copy_calibration(torch):
 
 
 def attn_source_hash() -> str:
+    import importlib.util
     h = hashlib.sha256()
     for f in ATTN_SRCS:
         h.update(open(f, "rb").read())
+    spec = importlib.util.spec_from_file_location(
+        "attn_loop_gen", os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", "attn_loop_gen.py"))
+    gen = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(gen)
+    h.update("\n".join(gen.generate()).encode())
+    h.update(gen.clobber_list().encode())
     return h.hexdigest()[:16]
 
 

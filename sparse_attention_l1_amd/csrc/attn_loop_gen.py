@@ -28,7 +28,8 @@ blocks travel global -> LDS by buffer loads with an LDS destination (rows past t
 are out of the descriptor's range and read as zero); V tile j holds blocks 4j..4j+3, K tile j
 blocks 4j+2..4j+5, and one barrier every 4 steps (s = 3 mod 4) refills the two buffers freed
 since the last one.  The loop body is unrolled over 8 steps so that every LDS offset is an
-immediate.
+immediate.  The rare-path and ragged-block routines are called from stubs out of line, so
+each step's four tests fall through branches that are not taken.
 
 Row sums: the pair sums x + y of the exponentials (fp32, before the bf16 rounding that P gets
 for the MFMA) are added as a tree, (ps0 + ps1) + (ps2 + ps3) per half block.
