@@ -112,3 +112,24 @@ def test_iteration_graph_replays_match_eager(hs, fused):
         # eager work between replays, on the same buffers the graph reads
         hs.hsa_attention_active(st["q"], st["k_cache"], st["v_cache"], side, 0.5)
         torch.cuda.synchronize()
+
+
+def test_iteration_on_a_side_stream_matches(hs):
+    """Every launch goes to the caller's stream: the iteration issued on a side stream (default
+    priority) gives the same bits as on the current stream."""
+    st, na = _state(hs)
+    st["q_proj"].zero_()
+    st["out"].zero_()
+    initial = {k: t.clone() for k, t in st.items()}
+    _iteration(hs, st, fused=False)
+    torch.cuda.synchronize()
+    want = {k: st[k].clone() for k in OUTPUTS}
+    for k, t in initial.items():
+        st[k].copy_(t)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        _iteration(hs, st, fused=False)
+    side.synchronize()
+    for k in OUTPUTS:
+        assert torch.equal(st[k], want[k]), f"{k} differs on the side stream"
