@@ -10,11 +10,10 @@ import torch
 
 import oracle
 from sparse_attention_l1_amd import synth
-from tests.gpu_helpers import SyntheticModel, bf16_to_f64, bits_dev, dev, host, host_bits
+from tests.gpu_helpers import (SyntheticModel, attn_close, bf16_to_f64, bits_dev, dev, host,
+                                host_bits, velocities)
 
 pytestmark = pytest.mark.gpu
-
-ATOL = 2e-2
 
 
 @pytest.fixture(scope="module")
@@ -23,46 +22,7 @@ def hs():
     return hsastep
 
 
-def attn_close(got_bits, want, label, absolute=True):
-    """absolute: the 2e-2 max-abs bar (unit-variance inputs, |O| well below 1).  For peaky
-    softmaxes |O| reaches the range where one bf16 output ulp alone is 2^-7 * |O| (0.0156 at
-    |O| = 4), so only the resolution-relative bound 2^-7 * max|O| + 2e-3 applies there."""
-    got = bf16_to_f64(got_bits)
-    err = np.abs(got - want)
-    mx = float(np.max(np.abs(want))) if want.size else 0.0
-    worst = float(err.max()) if err.size else 0.0
-    print(f"[{label}] attention max-abs err {worst:.3e}, max|O| {mx:.3e}", flush=True)
-    if absolute:
-        assert worst <= ATOL
-    assert worst <= 2.0 ** -7 * mx + 2e-3
-
-
 # ----------------------------------------------------------------------------- selection
-
-def velocities(kind, n, c, seed):
-    r = np.random.default_rng(seed)
-    vp = r.standard_normal((n, c)).astype(np.float32)
-    if kind == "ties":
-        vp = np.ones((n, c), np.float32)
-        return vp, (vp * np.float32(1.25)).astype(np.float32)
-    if kind == "levels":
-        # r is exactly one of 4 values: long runs of equal keys across many workgroups
-        vp = np.ones((n, c), np.float32)
-        lv = np.array([0.0, 0.5, 1.0, 2.0], np.float32)[r.integers(0, 4, n)]
-        return vp, (vp + lv[:, None]).astype(np.float32)
-    if kind == "heavy":
-        lam = np.abs(r.standard_t(3, n)).astype(np.float32)
-    else:
-        lam = r.lognormal(0, 1, n).astype(np.float32)
-    vc = (vp + lam[:, None] * r.standard_normal((n, c)).astype(np.float32)).astype(np.float32)
-    if kind == "special":
-        vp[::7] = 0
-        vc[::14] = 0                # 0/0 rows
-        vc[3::11, 0] = np.nan       # NaN rows
-        vc[5::13] = vp[5::13]       # zero change
-        vp[6::17, :] *= np.float32(2.0 ** -130)   # denormal magnitudes
-    return vp, vc
-
 
 SELECT_CASES = [
     ("lognormal", 256, 16, (128, 128)),

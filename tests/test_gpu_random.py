@@ -13,8 +13,7 @@ import torch
 
 import oracle
 from sparse_attention_l1_amd import synth
-from tests.gpu_helpers import bits_dev, dev, host, host_bits
-from tests.test_gpu_parity import attn_close, velocities
+from tests.gpu_helpers import attn_close, bits_dev, dev, host, host_bits, velocities
 
 pytestmark = pytest.mark.gpu
 
