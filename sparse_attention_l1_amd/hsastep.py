@@ -162,6 +162,8 @@ def hsa_kv_update(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Ten
         raise ValueError("shape mismatch")
     if n_active > 0 and (k_new.shape[1] != n_active):
         raise ValueError("k_new / v_new must hold exactly n_active rows per batch entry")
+    if n_active < 0 or n_active > N or active_idx.numel() < n_active:
+        raise ValueError("need 0 <= n_active <= n_tokens and active_idx with >= n_active entries")
     _check(lib.hsa_kv_update(_dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
                              _dev(k_new, "k_new", _BF16), _dev(v_new, "v_new", _BF16),
                              _dev(active_idx, "active_idx", (torch.int32,)), n_active, N, B, H, D,
@@ -191,9 +193,13 @@ def hsa_qkv_project(x_active: torch.Tensor, w_qkv: torch.Tensor, bias: Optional[
             x_active.shape[0] != B or q_out.shape[0] != B or q_out.shape[2:] != (H, D) or \
             (bias is not None and bias.shape != (3 * H * D,)):
         raise ValueError("shape mismatch")
-    if x_active.shape[1] != n_active or q_out.shape[1] != n_active:
-        if B != 1:
-            raise ValueError("with batch > 1, x_active and q_out must hold exactly n_active rows")
+    if n_active < 0 or n_active > N or active_idx.numel() < n_active:
+        raise ValueError("need 0 <= n_active <= n_tokens and active_idx with >= n_active entries")
+    if x_active.shape[1] < n_active or q_out.shape[1] < n_active:
+        raise ValueError("x_active and q_out must hold at least n_active rows")
+    if B != 1 and (x_active.shape[1] != n_active or q_out.shape[1] != n_active):
+        # rows of batch entry b start at b * n_active, so the row stride must be n_active
+        raise ValueError("with batch > 1, x_active and q_out must hold exactly n_active rows")
     _check(lib.hsa_qkv_project(
         _dev(x_active, "x_active", _BF16), _dev(w_qkv, "w_qkv", _BF16),
         None if bias is None else _dev(bias, "bias", _BF16), _dev(q_out, "q_out", _BF16),

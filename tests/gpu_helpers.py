@@ -63,22 +63,21 @@ class SyntheticModel:
         return p, p
 
 
-# attention bar of the parity tests: max-abs against the float64 oracle
+# attention bar of the parity tests: max-abs against the float64 oracle, for every input
+# (unit-variance and peaky softmaxes alike).  Rounding the output to bf16 alone errs by at most
+# half an ulp, 2^-8 * |O| for |O| in [2^k, 2^(k+1)) with the ulp taken at 2^k (0.0156 just below
+# |O| = 8); the kernels' normaliser is the sum of the same rounded P that weights V, so a key
+# that dominates the softmax carries no rounding error of its own.
 ATOL = 2e-2
 
 
-def attn_close(got_bits, want, label, absolute=True):
-    """absolute: the 2e-2 max-abs bar (unit-variance inputs, |O| well below 1).  For peaky
-    softmaxes |O| reaches the range where one bf16 output ulp alone is 2^-7 * |O| (0.0156 at
-    |O| = 4), so only the resolution-relative bound 2^-7 * max|O| + 2e-3 applies there."""
+def attn_close(got_bits, want, label):
     got = bf16_to_f64(got_bits)
     err = np.abs(got - want)
     mx = float(np.max(np.abs(want))) if want.size else 0.0
     worst = float(err.max()) if err.size else 0.0
     print(f"[{label}] attention max-abs err {worst:.3e}, max|O| {mx:.3e}", flush=True)
-    if absolute:
-        assert worst <= ATOL
-    assert worst <= 2.0 ** -7 * mx + 2e-3
+    assert worst <= ATOL
 
 
 def velocities(kind, n, c, seed):

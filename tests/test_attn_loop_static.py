@@ -29,9 +29,11 @@ def test_lds_offsets_in_bounds():
 def test_loop_shape():
     body = GEN.generate()
     mf = [l for l in body if l.startswith("v_mfma")]
-    # per step: 16 S^T MFMAs (two chains of 8) and 16 P.V MFMAs; 8 unrolled steps
+    # per step: 16 S^T MFMAs (two chains of 8), 16 P.V MFMAs, and two row-sum MFMAs for each
+    # of the two blocks whose softmax ends in the step; 8 unrolled steps
     loop = body[body.index(".Lloop:"):body.index("s_branch .Lloop")]
-    assert sum(l.startswith("v_mfma") for l in loop) == 8 * 32
+    assert sum(l.startswith("v_mfma_f32_32x32x16_bf16") for l in loop) == 8 * 32
+    assert sum(l.startswith("v_mfma_f32_16x16x32_bf16") for l in loop) == 8 * 4
     assert sum(l == "s_barrier" for l in loop) == 2                  # one per 4 steps
     assert sum(l.startswith("buffer_load") for l in loop) == 2 * 16  # V and K tile per barrier
     assert sum(l.startswith("v_exp_f32") for l in loop) == 8 * 2 * 16
@@ -89,3 +91,39 @@ def test_checker_catches_an_undeclared_register():
         assert any("('v', 100)" in e for e in lc.check_registers(GEN, HIP))
     finally:
         GEN.clobbered = orig
+
+
+def test_checker_catches_an_early_block_sum_read():
+    # the range check reading a block sum before its row-sum MFMA has finished
+    def early(f):
+        def g(r):
+            out = f(r)
+            i = out.index("s_nop 3")
+            return out[:i - 1] + out[i + 1:]
+        return g
+    errs = _with_patch("step", early)
+    assert any("needs 12" in e for e in errs)
+
+
+def test_row_sum_operand_pattern():
+    """The A operand of the row-sum MFMA (lane l holds ones iff bit 2 of l equals bit 4) makes
+    every lane's result its own query's sum over the block's 32 keys.  Checked with the
+    16x16x32 operand layouts (A: lane l row l%16, k-group l/16; B: lane l column l%16, k-group
+    l/16; result: lane l column l%16, rows 4(l/16)..+3) and the S^T layout (lane q + 32g holds
+    query q)."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    lane = np.arange(64)
+    ones = (((lane >> 2) & 1) == ((lane >> 4) & 1)).astype(np.float64)
+    pvals = rng.random((64, 8))                # 8 packed P values held by each lane
+    A = np.zeros((16, 32))
+    B = np.zeros((32, 16))
+    for l in range(64):
+        A[l % 16, 8 * (l // 16):8 * (l // 16) + 8] = ones[l]
+        B[8 * (l // 16):8 * (l // 16) + 8, l % 16] = pvals[l]
+    D = A @ B
+    query = lane % 32                           # S^T accumulator: lane q + 32g holds query q
+    want = np.array([pvals[query == q].sum() for q in range(32)])
+    for l in range(64):
+        got = D[4 * (l // 16):4 * (l // 16) + 4, l % 16]
+        assert np.allclose(got, want[query[l]])

@@ -2,7 +2,7 @@
 
 Bars: group ids, scores, active index lists, cache rows and the Euler state are
 bit-exact; attention (bf16 in/out, fp32 accumulation) is within max-abs 2e-2 of
-the float64 oracle, and also within 2^-7 * max|O| + 2e-3.
+the float64 oracle for every input, peaky softmaxes included.
 """
 import numpy as np
 import pytest
@@ -141,6 +141,11 @@ ATTN_CASES = [
     (1, 257, 1000, 1, 128, 1.0),    # a second query tile holding one query
     (1, 100, 900, 2, 128, 16.0),    # very peaky
     (1, 64, 2000, 40, 128, 1.0),    # 40 heads (token stride 10 KB)
+    (2, 130, 5000, 2, 128, 8.0),    # peaky, both kernels' batch path
+    (1, 64, 4000, 3, 64, 16.0),     # very peaky, head_dim 64
+    (1, 300, 32760, 1, 128, 16.0),  # very peaky over the single-step key count
+    (1, 100, 3000, 2, 128, 32.0),   # one key dominates almost every query
+    (1, 100, 200, 2, 128, 32.0),    # the same on the short-cache kernel
 ]
 
 
@@ -157,7 +162,7 @@ def test_attention(hs, B, A, N, H, D, qs):
     o = out[: B * A * H * D].view(B, A, H, D)
     hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
     torch.cuda.synchronize()
-    attn_close(host_bits(o), want, f"B{B} A{A} N{N} H{H} D{D} x{qs}", absolute=qs == 1.0)
+    attn_close(host_bits(o), want, f"B{B} A{A} N{N} H{H} D{D} x{qs}")
     assert bool((out[B * A * H * D:] == 0x7F7F).all())
     # determinism, and independence of a query from its tile neighbours
     o2 = torch.empty_like(o)
