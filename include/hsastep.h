@@ -125,6 +125,25 @@ int hsa_active_set(const int32_t* group_id, int64_t n_tokens, const int32_t* bud
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hsa_active_set without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, result, validation and errors as hsa_active_set, minus the workspace.  The
+ * per-chunk counts live in the library's own device array (one word per 1024 tokens, 64 KB),
+ * resident on every device the library runs on until the process ends; its address is looked
+ * up on the first call on each device, so make that first call outside a graph capture.
+ * Every call on one device shares that array: calls that overlap on one device (other streams,
+ * other threads) race and must be ordered by the caller.  Calls allocate nothing and clear
+ * nothing (each call writes every count it reads).
+ * Limit: n_tokens <= HSASTEP_NOALLOC_MAX_TOKENS, else HSASTEP_ERR_UNSUPPORTED.
+ */
+#define HSASTEP_NOALLOC_MAX_TOKENS (1 << 24)
+int hsa_active_set_noalloc(const int32_t* group_id, int64_t n_tokens,
+                           const int32_t* budgets_host, const int64_t* group_sizes_host,
+                           int32_t n_groups, int32_t T, int32_t m, int32_t iter,
+                           int32_t* active_idx, int32_t* active_pos, int64_t* n_active_host,
+                           void* stream);
+
+/*
  * Row gather: dst[a] = src[index[a]] for a < n_rows, rows of row_bytes bytes.
  * Used for the model input of the active tokens (their latent rows) and any
  * per-token state ([HSA-nl] §2.2 item 1: only the active tokens enter the

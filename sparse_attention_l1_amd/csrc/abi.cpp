@@ -14,6 +14,9 @@
 
 #define HSASTEP_API extern "C" __attribute__((visibility("default")))
 
+static_assert(HSASTEP_NOALLOC_MAX_TOKENS == hsastep::kNoAllocMaxTokens,
+              "the header's limit of hsa_active_set_noalloc must match its scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -129,6 +132,32 @@ HSASTEP_API int hsa_active_set(const int32_t* group_id, int64_t n_tokens,
   *n_active_host = hsastep::n_active_from_mask(mask, group_sizes_host, n_groups);
   int32_t* blockcnt =
       reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.blockcnt_off);
+  return hip_status(hsastep::launch_active(group_id, n_tokens, mask, n_groups, active_idx,
+                                           active_pos, blockcnt, as_stream(stream)),
+                    "active set");
+}
+
+HSASTEP_API int hsa_active_set_noalloc(const int32_t* group_id, int64_t n_tokens,
+                                       const int32_t* budgets_host,
+                                       const int64_t* group_sizes_host, int32_t n_groups,
+                                       int32_t T, int32_t m, int32_t iter, int32_t* active_idx,
+                                       int32_t* active_pos, int64_t* n_active_host,
+                                       void* stream) {
+  std::string msg;
+  if (hsastep::check_schedule(n_tokens, budgets_host, group_sizes_host, n_groups, T, m, msg))
+    return fail(HSASTEP_ERR_ARG, msg);
+  if (n_tokens > HSASTEP_NOALLOC_MAX_TOKENS)
+    return fail(HSASTEP_ERR_UNSUPPORTED,
+                "hsa_active_set_noalloc: n_tokens above HSASTEP_NOALLOC_MAX_TOKENS (2^24); "
+                "use hsa_active_set with a workspace");
+  if (iter < 0 || iter >= T) return fail(HSASTEP_ERR_ARG, "iter must be in [0, T)");
+  if (!group_id || !active_idx || !active_pos || !n_active_host)
+    return fail(HSASTEP_ERR_ARG, "null pointer argument");
+  int32_t* blockcnt = nullptr;
+  if (int rc = hip_status(hsastep::active_scratch(&blockcnt), "active-set scratch address"))
+    return rc;
+  const uint32_t mask = hsastep::group_active_mask(budgets_host, n_groups, T, m, iter);
+  *n_active_host = hsastep::n_active_from_mask(mask, group_sizes_host, n_groups);
   return hip_status(hsastep::launch_active(group_id, n_tokens, mask, n_groups, active_idx,
                                            active_pos, blockcnt, as_stream(stream)),
                     "active set");

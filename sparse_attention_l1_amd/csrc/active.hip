@@ -11,6 +11,8 @@
 // Two launches instead of one chained scan: no workgroup ever waits on another.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "host.hpp"
 #include "kernels.hpp"
 
@@ -101,7 +103,34 @@ __global__ __launch_bounds__(kThreads) void active_compact_kernel(
   }
 }
 
+// Per-chunk counts of hsa_active_set_noalloc, for callers that cannot allocate: one word per
+// 1024-token chunk up to kNoAllocMaxTokens tokens (64 KB), resident on every device the
+// library runs on until the process ends.  Host code never passes this name to a kernel (on
+// the host it is only a stand-in); it uses the device address hipGetSymbolAddress returns.
+constexpr int64_t kScratchWords = kNoAllocMaxTokens / kActiveBlockTokens + 1;
+static __device__ __align__(256) int32_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t active_scratch(int32_t** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_active(const int32_t* group_id, int64_t n_tokens, uint32_t group_mask,
                          int n_groups, int32_t* active_idx, int32_t* active_pos, int32_t* blockcnt,

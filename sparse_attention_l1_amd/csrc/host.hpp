@@ -16,6 +16,7 @@ namespace hsastep {
 constexpr int kMaxGroups = 16;
 constexpr int kMaxChannels = 256;
 constexpr int kActiveBlockTokens = 1024;   // tokens per workgroup of the active-set kernels
+constexpr int64_t kNoAllocMaxTokens = int64_t(1) << 24;   // limit of hsa_active_set_noalloc
 constexpr int kRankThreads = 512;          // threads per workgroup of the grouping kernels
 constexpr int kRankChunk = 512;            // tokens a grouping workgroup holds at once
 constexpr int kRankMaxBlocks = 512;        // cap on grouping workgroups (bounds the workspace)

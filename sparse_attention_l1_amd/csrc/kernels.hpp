@@ -24,6 +24,11 @@ hipError_t launch_active(const int32_t* group_id, int64_t n_tokens, uint32_t gro
                          int n_groups, int32_t* active_idx, int32_t* active_pos, int32_t* blockcnt,
                          hipStream_t stream);
 
+// active.hip: device address of the library's own per-chunk count array on the current device
+// (kNoAllocMaxTokens / 1024 + 1 words), looked up once per device; for callers that cannot
+// allocate.  Calls that use it and overlap on one device race.
+hipError_t active_scratch(int32_t** ptr);
+
 // rows.hip: row gather and the KV-cache row scatter.
 hipError_t launch_gather(void* dst, const void* src, const int32_t* index, int64_t n_rows,
                          int64_t n_src_rows, int64_t row_bytes, hipStream_t stream);

@@ -32,6 +32,8 @@ _SIGS = {
     "hsa_select_groups": ([_p, _p, _i64, _i32, _p, _i32, _p, _p, _p, _sz, _p], ctypes.c_int),
     "hsa_active_set": ([_p, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p],
                        ctypes.c_int),
+    "hsa_active_set_noalloc": ([_p, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p],
+                               ctypes.c_int),
     "hsastep_gather_rows": ([_p, _p, _p, _i64, _i64, _i64, _p], ctypes.c_int),
     "hsa_kv_update": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p], ctypes.c_int),
     "hsa_attention_active": ([_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _f, _p], ctypes.c_int),
@@ -46,6 +48,7 @@ for _name, (_args, _ret) in _SIGS.items():
 EXPORTED = tuple(_SIGS)
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
+NOALLOC_MAX_TOKENS = 1 << 24      # HSASTEP_NOALLOC_MAX_TOKENS
 
 
 class HsaStepError(RuntimeError):
@@ -137,6 +140,24 @@ def hsa_active_set(group_id: torch.Tensor, budgets: Sequence[int], group_sizes: 
         len(budgets), T, m, iteration, _dev(active_idx, "active_idx", (torch.int32,)),
         _dev(active_pos, "active_pos", (torch.int32,)), ctypes.byref(out),
         _dev(ws, "workspace", (torch.uint8,)), ws.numel(), _stream(stream)), "hsa_active_set")
+    return out.value
+
+
+def hsa_active_set_noalloc(group_id: torch.Tensor, budgets: Sequence[int],
+                           group_sizes: Sequence[int], T: int, m: int, iteration: int,
+                           active_idx: torch.Tensor, active_pos: torch.Tensor,
+                           stream=None) -> int:
+    """hsa_active_set with the library's own device scratch in place of a workspace (for
+    callers that cannot allocate); calls that overlap on one device race."""
+    n = group_id.shape[0]
+    if active_idx.shape != (n,) or active_pos.shape != (n,):
+        raise ValueError("active_idx and active_pos must have n_tokens entries")
+    out = ctypes.c_int64(0)
+    _check(lib.hsa_active_set_noalloc(
+        _dev(group_id, "group_id", (torch.int32,)), n, _host_i32(budgets), _host_i64(group_sizes),
+        len(budgets), T, m, iteration, _dev(active_idx, "active_idx", (torch.int32,)),
+        _dev(active_pos, "active_pos", (torch.int32,)), ctypes.byref(out), _stream(stream)),
+        "hsa_active_set_noalloc")
     return out.value
 
 

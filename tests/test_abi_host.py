@@ -105,6 +105,24 @@ def test_active_set_rejects(hs):
     assert b"divide" in hs.lib.hsastep_last_error()
 
 
+def test_active_set_noalloc_rejects_on_the_host(hs):
+    """Validation of the allocation-free variant runs before it looks up its scratch array
+    or enqueues anything: schedule errors, more tokens than the array covers, null pointers."""
+    def run(budgets, sizes, T, m, it, n=None, idx=FAKE):
+        b = (ctypes.c_int32 * len(budgets))(*budgets)
+        s = (ctypes.c_int64 * len(sizes))(*sizes)
+        n = sum(sizes) if n is None else n
+        out = ctypes.c_int64(-7)
+        return call(hs, "hsa_active_set_noalloc", FAKE, n, b, s, len(budgets), T, m, it, idx,
+                    FAKE, ctypes.byref(out), None)
+    assert run([40, 15], [5, 5], 40, 4, 5) == hs.ERR_ARG        # 15 does not divide 40
+    assert run([40, 20], [5, 5], 40, 4, 40) == hs.ERR_ARG       # iter >= T
+    assert run([40, 20], [5, 5], 40, 4, 5, idx=None) == hs.ERR_ARG
+    big = hs.NOALLOC_MAX_TOKENS + 1
+    assert run([40, 20], [big - 5, 5], 40, 4, 5) == hs.ERR_UNSUPPORTED
+    assert b"HSASTEP_NOALLOC_MAX_TOKENS" in hs.lib.hsastep_last_error()
+
+
 def test_kv_attention_euler_gather_reject(hs):
     kv = lambda *a: call(hs, "hsa_kv_update", *a)
     assert kv(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 4, 1, 2, 64, None) == hs.ERR_ARG   # n_active > N
