@@ -15,8 +15,7 @@ matrix cores if it is spread evenly between the MFMAs of the same wave.
 
 Key blocks are 32 keys (block x).  Step s of the loop has two halves of 16 MFMA slots:
 
-  H1(s): the S^T chains S(s+1, 1) and S(s+2, 0), interleaved (two independent accumulators),
-         plus the row-sum MFMAs of the two blocks whose softmax ends here (below)
+  H1(s): the S^T chains S(s+1, 1) and S(s+2, 0), interleaved (two independent accumulators)
          VALU: pairs 4..7 of softmax(s+1, 0) and softmax(s, 1), then their range checks
          LDS:  the 16 transposing reads of V(s+1)
   H2(s): the P.V groups PV(s, 1) and PV(s+1, 0), interleaved
@@ -34,18 +33,17 @@ each step's four tests fall through branches that are not taken.
 
 Row sums: the normaliser of a query is the sum of the bf16-rounded P that the P.V MFMAs
 consume, so a key that dominates the softmax is weighted by exactly p / sum(p) whatever the
-rounding of p.  Two 16x16x32 bf16 MFMAs per 32-key block form it from the packed P registers:
-the A operand is a constant 0/1 pattern (lane l holds ones iff bit 2 of l equals bit 4 of l),
-under which the 16x16 result row 4j..4j+3 of column n collects the P values of the lanes that
-hold query n (j even) or query n + 16 (j odd), so every lane ends with its own query's sum over
-all 32 keys of the block, in register 0 of the 4-register result.  The first MFMA (P registers
-0..3, pairs 0..3) goes at the start of H1, the second (pairs 4..7) after the slot that finishes
-the block's exponentials; the range check and L += sum follow at the end of H1.
+rounding of p.  After each pair is rounded into its packed register, the two bf16 halves are
+read back as fp32 (the high half by masking off the low 16 bits, the low half by a 16-bit left
+shift) and added; the four pair sums of a half block are added as a tree, (ps0 + ps1) +
+(ps2 + ps3), into this lane's block sum.  A lane holds 16 of a query's 32 keys per block, so
+the running sum is per lane; the two lanes of a query add theirs at the end.  (Row sums by
+16x16x32 or 4x4x4 MFMAs on the packed P, with a 0/1 operand, cost 11-19% of the kernel's time:
+more than these 24 extra VALU instructions per block.)
 
 Register map (per lane):  VGPR  S 0-63, P 64-95, K fragments 96-159, LDS/buffer addresses
-160-183, softmax state 184-192, temps 196-218, block sums 220-227, ones pattern 228-231;
-AGPR  O 0-127, Q^T 128-191, V^T fragments 192-255;  SGPR 40-77 (descriptors, counters,
-routine addresses).
+160-183, softmax state 184-194, temps 196-218;  AGPR  O 0-127, Q^T 128-191, V^T fragments
+192-255;  SGPR 40-77 (descriptors, counters, routine addresses).
 """
 import sys
 
@@ -60,18 +58,16 @@ KADDR = 160                # 8: LDS byte address of K fragment u (block 0 of buf
 VADDR = 168                # 8: [hh*4 + e] LDS byte address of a V transposing read
 VOFF = 176                 # 8: buffer offset of tile-load instruction i
 M = 184                    # +qb reference max (log2 units)
-L = 186                    # +qb running sum of the query's rounded P (both lanes hold it)
+L = 186                    # +qb running sum of the rounded P (this lane's half of the keys)
 NEGM = 188                 # +qb  -M
 VAX = 190                  # (lane ^ 32) * 4, ds_bpermute address of the partner lane
 VT = 191                   # 4*g - lim for the ragged last block
 VNINF = 192                # -inf
+LS = 193                   # +qb block sum (this lane's 16 keys)
 def TMP(qb):               # 8 softmax temps (4 pairs in flight) per query block
     return 196 + qb * 9
 T0 = 214                   # rare-path temps T0..T0+4
-def RS(qb):                # block sum of the rounded P (16x16x32 MFMA result, 4 VGPRs; reg 0 used)
-    return 220 + qb * 4
-ONES = 228                 # 4: A operand of the row-sum MFMA (constant 0/1 pattern, bf16)
-NV_END = 232
+NV_END = 219
 
 def O(qb, e):              # O^T accumulator (AGPR), 16 regs
     return (qb * 4 + e) * 16
@@ -103,7 +99,7 @@ TILE_BYTES = 32768
 BLK_BYTES = 8192           # 32 keys x 256 B
 
 # Inputs the kernel passes in pinned registers (operand constraints of the asm statement).
-PINNED_IN = {"v": set(range(160, 192)) | set(range(ONES, ONES + 4)), "a": set(range(0, 192)),
+PINNED_IN = {"v": set(range(160, 192)), "a": set(range(0, 192)),
              "s": {KDESC + i for i in range(4)} | {VDESC + i for i in range(4)} |
                   {SC, LAST, MASK1, M0BASE, ADV}}
 
@@ -166,8 +162,10 @@ def desc_advance(desc):
 
 
 def softmax_part(par, qb, t0, t1):
-    """Pairs t0..t0+3 of one softmax block: x, y = 2^(s*c - m); P[t] = bf16(x, y).  A pair's
-    conversion comes after the next pair's exponentials (one wait state after v_exp)."""
+    """Pairs t0..t0+3 of one softmax block: x, y = 2^(s*c - m); P[t] = bf16(x, y); the two
+    rounded halves of P[t] read back as fp32 and added (the pair sum of the values the MFMA
+    uses); the four pair sums added as a tree into LS (set by the first half, added to by the
+    second).  A pair's consumers come after the next pair's exponentials."""
     assert t1 == t0 + 4
     sb, pb, tmp = S(par, qb), P(par, qb), TMP(qb)
     ops = []
@@ -175,7 +173,10 @@ def softmax_part(par, qb, t0, t1):
         return tmp + 2 * (t % 4), tmp + 2 * (t % 4) + 1
     def finish(t):
         x, y = xy(t)
-        return [f"v_cvt_pk_bf16_f32 {v(pb + t)}, {v(x)}, {v(y)}"]
+        return [f"v_cvt_pk_bf16_f32 {v(pb + t)}, {v(x)}, {v(y)}",
+                f"v_and_b32 {v(y)}, 0xffff0000, {v(pb + t)}",
+                f"v_lshlrev_b32 {v(x)}, 16, {v(pb + t)}",
+                f"v_add_f32 {v(x)}, {v(x)}, {v(y)}"]
     pend = None
     for t in range(t0, t1):
         x, y = xy(t)
@@ -187,20 +188,15 @@ def softmax_part(par, qb, t0, t1):
             ops.extend(finish(pend))
         pend = t
     ops.extend(finish(pend))       # two instructions after the last exponential
+    x0, x1, x2, x3 = (xy(t)[0] for t in range(t0, t1))
+    ops.append(f"v_add_f32 {v(x0)}, {v(x0)}, {v(x1)}")
+    ops.append(f"v_add_f32 {v(x2)}, {v(x2)}, {v(x3)}")
+    if t0 == 0:
+        ops.append(f"v_add_f32 {v(LS + qb)}, {v(x0)}, {v(x2)}")
+    else:
+        ops.append(f"v_add_f32 {v(x0)}, {v(x0)}, {v(x2)}")
+        ops.append(f"v_add_f32 {v(LS + qb)}, {v(LS + qb)}, {v(x0)}")
     return ops
-
-
-def rowsum(par, qb, half):
-    """Row-sum MFMA over P registers 4*half..4*half+3 of block (par, qb) into RS(qb): the
-    first half starts the sum (src C = 0), the second adds to it."""
-    src_c = "0" if half == 0 else v(RS(qb), 4)
-    return (f"v_mfma_f32_16x16x32_bf16 {v(RS(qb), 4)}, {v(ONES, 4)}, "
-            f"{v(P(par, qb) + 4 * half, 4)}, {src_c}")
-
-
-def rowsum_full(par, qb):
-    """Both row-sum MFMAs of a block whose P is complete, and the wait for their result."""
-    return ["s_nop 1", rowsum(par, qb, 0), rowsum(par, qb, 1), "s_nop 7", "s_nop 3"]
 
 
 def softmax_full(par, qb):
@@ -220,20 +216,46 @@ def call_site(branch, routine_regs, label):
 
 
 def call_stubs(body):
+    """A stub calls its routine (or, for a pair check, each block's routine that its own range
+    check asks for) and branches back."""
     out = []
     for l in body:
         if l.endswith("_call") and l.startswith("s_cbranch"):
             label = l.split()[1][:-len("_call")]
-            out += [f"{label}_call:", f"s_swappc_b64 {s(RET, 2)}, {CALL_STUBS[label]}",
-                    f"s_branch {label}"]
+            stub = CALL_STUBS[label]
+            if isinstance(stub, str):
+                out += [f"{label}_call:", f"s_swappc_b64 {s(RET, 2)}, {stub}"]
+            else:
+                out.append(f"{label}_call:")
+                for k, (qb, regs) in enumerate(stub):
+                    out += [f"v_cmp_nge_f32 vcc, 0x43800000, {v(LS + qb)}",
+                            f"s_cbranch_vccz {label}_n{k}",
+                            f"s_swappc_b64 {s(RET, 2)}, {regs}",
+                            f"{label}_n{k}:"]
+            out.append(f"s_branch {label}")
     return out
 
 
 def check_and_fix(par, qb, label):
-    """Calls the rare path if any lane's block sum is not in (-inf, 256]; then L += sum."""
-    return ([f"v_cmp_nge_f32 vcc, 0x43800000, {v(RS(qb))}"] +
+    """Calls the rare path if any lane's block sum is not in (-inf, 256]; then L += LS."""
+    return ([f"v_cmp_nge_f32 vcc, 0x43800000, {v(LS + qb)}"] +
             call_site("s_cbranch_vccnz", s(FIXA + 2 * (par * 2 + qb), 2), label) +
-            [f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(RS(qb))}"])
+            [f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(LS + qb)}"])
+
+
+def check_pair_and_fix(blocks, label):
+    """Range check of two blocks with one branch: the two lanes' block sums are added (a sum
+    of non-negative values is in (-inf, 256] only if both are, and inf or NaN carries through),
+    and only if some lane's total is out of range does the stub test the blocks one by one and
+    call the rare path for each that needs it.  Then L += LS for both.  One data-dependent
+    branch per step instead of two: the second one cost 7% of the loop (measured on MI355X)."""
+    (pa, qa), (pb, qb) = blocks
+    CALL_STUBS[label] = [(qa, s(FIXA + 2 * (pa * 2 + qa), 2)), (qb, s(FIXA + 2 * (pb * 2 + qb), 2))]
+    return [f"v_add_f32 {v(T0)}, {v(LS + qa)}, {v(LS + qb)}",
+            f"v_cmp_nge_f32 vcc, 0x43800000, {v(T0)}",
+            f"s_cbranch_vccnz {label}_call", f"{label}:",
+            f"v_add_f32 {v(L + qa)}, {v(L + qa)}, {v(LS + qa)}",
+            f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(LS + qb)}"]
 
 
 def mask_call(par, qb, stepreg, label):
@@ -303,9 +325,7 @@ def step(r):
         mf.append(mfma_s(q, 1, u))
         mf.append(mfma_s(p, 0, u))
     reads = vreads(x1)
-    # the exponentials end by slot 13, so the second row-sum MFMAs go after slot 14's MFMA
-    # and their sums are ready (12 wait states) before the checks that end H1
-    plan = place(merge(softmax_part(q, 0, 4, 8), softmax_part(p, 1, 4, 8)), list(range(14)))
+    plan = place(merge(softmax_part(q, 0, 4, 8), softmax_part(p, 1, 4, 8)), list(range(16)))
     for k in range(16):
         if li < len(loads) and k % 2 == 1:
             out.append(loads[li][0])
@@ -313,28 +333,23 @@ def step(r):
         if k == 8:
             out.append("s_waitcnt lgkmcnt(7)")
         out.append(reads[k])
-        if k == 0:
-            out.extend([rowsum(q, 0, 0), rowsum(p, 1, 0)])
         out.extend(plan.get(k, []))
-        if k == 14:
-            out.extend([rowsum(q, 0, 1), rowsum(p, 1, 1)])
         if li < len(loads) and k % 2 == 1:
             out.append(loads[li][1])
             li += 1
-    out.extend(["s_nop 7", "s_nop 3"])
-    out.extend(check_and_fix(q, 0, f".Lf{r}a"))
-    out.extend(check_and_fix(p, 1, f".Lf{r}b"))
+    # the range checks of the two blocks whose softmax ends here, with one branch
+    out.extend(check_pair_and_fix(((q, 0), (p, 1)), f".Lf{r}"))
     # ---------------- H2: PV(s,1) [VF[p], P[p][1]] and PV(s+1,0) [VF[q], P[q][0]]
+    kr = [kread(x3, u) for u in range(8)]
+    valu = (mask_call(q, 1, MASK1, f".Lm{r}a") + mask_call(p, 0, MASK0, f".Lm{r}b") +
+            merge(softmax_part(q, 1, 0, 4), softmax_part(p, 0, 0, 4)))
+    plan = place(valu, list(range(1, 16)))
     out.append("s_waitcnt lgkmcnt(7)")       # V(s+1) reads 0..8 landed (h2 = 0 fragments)
     mf = []
     for h2 in range(2):
         for e in range(4):
             mf.append(mfma_pv(p, 1, e, h2))
             mf.append(mfma_pv(q, 0, e, h2))
-    kr = [kread(x3, u) for u in range(8)]
-    valu = (mask_call(q, 1, MASK1, f".Lm{r}a") + mask_call(p, 0, MASK0, f".Lm{r}b") +
-            merge(softmax_part(q, 1, 0, 4), softmax_part(p, 0, 0, 4)))
-    plan = place(valu, list(range(1, 16)))
     for k in range(16):
         if k == 9:
             out.append("s_waitcnt lgkmcnt(8)")   # all V(s+1) reads landed (h2 = 1 fragments)
@@ -397,7 +412,7 @@ def fix_routine(par, qb):
     out.append(f"v_mov_b32 {v(M + qb)}, {v(t4)}")
     out.append(f"v_xor_b32 {v(NEGM + qb)}, 0x80000000, {v(t4)}")
     out.extend(softmax_full(par, qb))
-    out.extend(rowsum_full(par, qb))
+    out.append("s_nop 1")
     out.append(f"s_setpc_b64 {s(RET, 2)}")
     return out
 
@@ -463,7 +478,6 @@ def prologue():
         out.extend(vr[2 * u:2 * u + 2])
     out += ["s_nop 7"]
     out.extend(softmax_full(0, 0))
-    out.extend(rowsum_full(0, 0))
     out.extend(check_and_fix(0, 0, ".Lfp0"))
     out.append("s_waitcnt lgkmcnt(0)")
     out.append("s_nop 1")
@@ -487,7 +501,6 @@ def epilogue():
         out.append(f".Lexit{x}:")
         out.append("s_waitcnt lgkmcnt(0)")
         out.extend(softmax_part(x, 1, 4, 8))
-        out.extend(rowsum_full(x, 1))
         out.extend(check_and_fix(x, 1, f".Lfe{x}"))
         out.append("s_nop 1")
         for h2 in range(2):
@@ -521,7 +534,7 @@ def generate():
 
 def clobbered():
     """Registers the body writes besides its in/out operands: {'v': set, 'a': set, 's': set}."""
-    return {"v": set(range(0, 160)) | (set(range(192, ONES)) - {195}),
+    return {"v": set(range(0, 160)) | (set(range(192, NV_END)) - {195}),
             "a": set(range(192, 256)),
             "s": {STEP, M0SAVE, MASK0, MASK0 + 1} | set(range(NINF, 76))}
 

@@ -187,10 +187,15 @@ def expand(gen, lines, body, take_calls):
         if take_calls and p and p[0] in ("s_cbranch_vccnz", "s_cbranch_scc1") and \
                 p[1][0].endswith("_call"):
             stub = body.index(p[1][0] + ":")
-            call, back = body[stub + 1], body[stub + 2]
-            assert call.startswith("s_swappc_b64") and back == "s_branch " + p[1][0][:-5], \
-                f"malformed call stub {p[1][0]}"
-            out.extend(_call(gen, body, call))
+            back = "s_branch " + p[1][0][:-5]
+            j = stub + 1
+            while body[j] != back:           # the stub: its tests, every call taken
+                if body[j].startswith("s_swappc_b64"):
+                    out.extend(_call(gen, body, body[j]))
+                else:
+                    out.append(body[j])
+                j += 1
+                assert j < len(body), f"malformed call stub {p[1][0]}"
             out.append(back)
         elif take_calls and p and p[0] == "s_swappc_b64":
             out.extend(_call(gen, body, l)[1:])

@@ -6,6 +6,7 @@ offsets are checked here statically; a planted mistake of each kind must be caug
 """
 import os
 
+import numpy as np
 import pytest
 
 import loop_checker as lc
@@ -29,11 +30,13 @@ def test_lds_offsets_in_bounds():
 def test_loop_shape():
     body = GEN.generate()
     mf = [l for l in body if l.startswith("v_mfma")]
-    # per step: 16 S^T MFMAs (two chains of 8), 16 P.V MFMAs, and two row-sum MFMAs for each
-    # of the two blocks whose softmax ends in the step; 8 unrolled steps
+    # per step: 16 S^T MFMAs (two chains of 8) and 16 P.V MFMAs; 8 unrolled steps
     loop = body[body.index(".Lloop:"):body.index("s_branch .Lloop")]
     assert sum(l.startswith("v_mfma_f32_32x32x16_bf16") for l in loop) == 8 * 32
-    assert sum(l.startswith("v_mfma_f32_16x16x32_bf16") for l in loop) == 8 * 4
+    assert sum(l.startswith("v_mfma") for l in loop) == 8 * 32
+    # two blocks per step, 8 rounded pairs each, read back as two fp32 values
+    assert sum(l.startswith("v_and_b32") for l in loop) == 8 * 2 * 8
+    assert sum(l.startswith("v_lshlrev_b32") for l in loop) == 8 * 2 * 8
     assert sum(l == "s_barrier" for l in loop) == 2                  # one per 4 steps
     assert sum(l.startswith("buffer_load") for l in loop) == 2 * 16  # V and K tile per barrier
     assert sum(l.startswith("v_exp_f32") for l in loop) == 8 * 2 * 16
@@ -93,37 +96,76 @@ def test_checker_catches_an_undeclared_register():
         GEN.clobbered = orig
 
 
-def test_checker_catches_an_early_block_sum_read():
-    # the range check reading a block sum before its row-sum MFMA has finished
-    def early(f):
-        def g(r):
-            out = f(r)
-            i = out.index("s_nop 3")
-            return out[:i - 1] + out[i + 1:]
-        return g
-    errs = _with_patch("step", early)
-    assert any("needs 12" in e for e in errs)
+def _bf16_rne(x):
+    """fp32 -> bf16 bits, round to nearest even (finite inputs)."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint32)
 
 
-def test_row_sum_operand_pattern():
-    """The A operand of the row-sum MFMA (lane l holds ones iff bit 2 of l equals bit 4) makes
-    every lane's result its own query's sum over the block's 32 keys.  Checked with the
-    16x16x32 operand layouts (A: lane l row l%16, k-group l/16; B: lane l column l%16, k-group
-    l/16; result: lane l column l%16, rows 4(l/16)..+3) and the S^T layout (lane q + 32g holds
-    query q)."""
-    import numpy as np
-    rng = np.random.default_rng(0)
-    lane = np.arange(64)
-    ones = (((lane >> 2) & 1) == ((lane >> 4) & 1)).astype(np.float64)
-    pvals = rng.random((64, 8))                # 8 packed P values held by each lane
-    A = np.zeros((16, 32))
-    B = np.zeros((32, 16))
-    for l in range(64):
-        A[l % 16, 8 * (l // 16):8 * (l // 16) + 8] = ones[l]
-        B[8 * (l // 16):8 * (l // 16) + 8, l % 16] = pvals[l]
-    D = A @ B
-    query = lane % 32                           # S^T accumulator: lane q + 32g holds query q
-    want = np.array([pvals[query == q].sum() for q in range(32)])
-    for l in range(64):
-        got = D[4 * (l // 16):4 * (l // 16) + 4, l % 16]
-        assert np.allclose(got, want[query[l]])
+def _run_valu(ops, reg, sgpr):
+    """Executes the softmax's VALU instructions on one lane (register contents as uint32 bits):
+    fp32 FMA/add, exp2, RNE bf16 packing, and the integer read-back of the packed halves."""
+    f = lambda r: np.uint32(reg[r]).view(np.float32)
+    put = lambda r, x: reg.__setitem__(r, int(np.float32(x).view(np.uint32)))
+    num = lambda t: int(t[1:]) if t.startswith("v") else None
+    for op in ops:
+        name, rest = op.split(None, 1)
+        a = [t.strip() for t in rest.split(",")]
+        if name == "v_fma_f32":
+            sc = np.uint32(sgpr[int(a[2][1:])]).view(np.float32)
+            put(num(a[0]), np.float32(np.float64(f(num(a[1]))) * np.float64(sc) + np.float64(f(num(a[3])))))
+        elif name == "v_exp_f32":
+            put(num(a[0]), np.exp2(f(num(a[1]))))
+        elif name == "v_cvt_pk_bf16_f32":
+            lo, hi = _bf16_rne(f(num(a[1]))), _bf16_rne(f(num(a[2])))
+            reg[num(a[0])] = int(lo) | (int(hi) << 16)
+        elif name == "v_and_b32":
+            reg[num(a[0])] = int(a[1], 16) & reg[num(a[2])]
+        elif name == "v_lshlrev_b32":
+            reg[num(a[0])] = (reg[num(a[2])] << int(a[1])) & 0xFFFFFFFF
+        elif name == "v_add_f32":
+            put(num(a[0]), f(num(a[1])) + f(num(a[2])))
+        else:
+            raise AssertionError(op)
+
+
+def test_block_sum_is_the_sum_of_the_rounded_p():
+    """The generated softmax of a block leaves in LS the fp32 tree sum of exactly the bf16
+    values written into its P registers (the weights the P.V MFMAs apply), and P holds
+    bf16(2^(s*c - m)) for the block's 16 scores of this lane."""
+    rng = np.random.default_rng(5)
+    for par, qb in ((0, 0), (1, 1), (0, 1)):
+        reg = {}
+        sc = np.float32(0.1275)
+        scores = (rng.standard_normal(16) * 20).astype(np.float32)
+        m = np.float32(scores.max() * sc - 3.0)
+        for j in range(16):
+            reg[GEN.S(par, qb) + j] = int(scores[j].view(np.uint32))
+        reg[GEN.NEGM + qb] = int(np.float32(-m).view(np.uint32))
+        _run_valu(GEN.softmax_full(par, qb), reg, {GEN.SC: int(sc.view(np.uint32))})
+        pbits = [reg[GEN.P(par, qb) + t] for t in range(8)]
+        vals = []
+        for w in pbits:
+            vals += [np.uint32((w & 0xFFFF) << 16).view(np.float32),
+                     np.uint32(w & 0xFFFF0000).view(np.float32)]
+        want_bits = _bf16_rne(np.exp2(np.float32(np.float64(scores) * np.float64(sc) - np.float64(m))))
+        got_bits = np.array([(w >> (16 * h)) & 0xFFFF for w in pbits for h in (0, 1)], np.uint32)
+        assert np.array_equal(got_bits, want_bits)
+        ps = [vals[2 * t] + vals[2 * t + 1] for t in range(8)]
+        tree = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]))
+        assert np.uint32(reg[GEN.LS + qb]) == np.float32(tree).view(np.uint32)
+
+
+def test_checker_catches_a_sum_of_unrounded_exponentials():
+    """Planted mistake: the pair sum taken from the fp32 exponentials instead of the rounded
+    pair fails the block-sum check above."""
+    orig = GEN.softmax_part
+    def bad(par, qb, t0, t1):
+        return [l for l in orig(par, qb, t0, t1)
+                if not l.startswith(("v_and_b32", "v_lshlrev_b32"))]
+    GEN.softmax_part = bad
+    try:
+        with pytest.raises(AssertionError):
+            test_block_sum_is_the_sum_of_the_rounded_p()
+    finally:
+        GEN.softmax_part = orig
