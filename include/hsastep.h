@@ -186,6 +186,41 @@ int hsa_attention_active(const uint16_t* q_active, const uint16_t* k_cache,
                          float softmax_scale, void* stream);
 
 /*
+ * hsa_attention_active with a caller workspace, for small or ragged active sets ([HSA-nl]
+ * §2.2 item 4: the cost is O(|A_i| * N), so iterations with few active tokens launch few
+ * query tiles).  Same operation, arguments, layouts and errors as hsa_attention_active, plus:
+ *
+ *   workspace          device buffer (16-byte aligned) of workspace_bytes bytes, or NULL with
+ *                      workspace_bytes == 0 (then it runs exactly as hsa_attention_active);
+ *                      contents on entry do not matter; overwritten
+ *   workspace_bytes    hsastep_attention_workspace_bytes(...) lets every plan run; a smaller
+ *                      buffer limits the plan to what fits
+ *
+ * With head_dim 128 and n_tokens >= 512, when the query tiles of the launch do not fill the
+ * last round of the device's compute units, the tiles of that round are split into up to 8
+ * key ranges that run as separate workgroups, and a second kernel merges their partial
+ * results (per query: unnormalised O, reference max and row sum of the rounded P, combined
+ * in fp32).  The result equals the unsplit computation up to fp32 rounding and the final
+ * bf16 rounding.  Calls on different streams need different workspaces.
+ */
+size_t hsastep_attention_workspace_bytes(int64_t n_active, int64_t n_tokens, int32_t batch,
+                                         int32_t heads, int32_t head_dim);
+/* The plan hsa_attention_active_ws follows for a launch on a device with compute_units
+ * compute units and a workspace of workspace_bytes bytes (host only, no device work):
+ * plan_host[4] = {whole tiles, split tiles, key ranges per split tile, keys per range}, tiles
+ * of 256 queries of one (batch, head).  {0, 0, 0, 0} when the shape takes the kernel without
+ * splits (head_dim 64 or fewer than 256 keys); {tiles, 0, 1, 0} when splitting would not
+ * shorten the launch or nothing fits in the workspace. */
+int hsastep_attention_plan(int64_t n_active, int64_t n_tokens, int32_t batch, int32_t heads,
+                           int32_t head_dim, int32_t compute_units, size_t workspace_bytes,
+                           int32_t* plan_host);
+int hsa_attention_active_ws(const uint16_t* q_active, const uint16_t* k_cache,
+                            const uint16_t* v_cache, uint16_t* out, int64_t n_active,
+                            int64_t n_tokens, int32_t batch, int32_t heads, int32_t head_dim,
+                            float softmax_scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * Fused QKV projection of the active tokens with the cache write as its epilogue
  * ([HSA-nl] §2.2 items 1-2: only the active tokens go through the model's projections,
  * and their fresh K and V rows overwrite their cache slots).  With HD = heads*head_dim,

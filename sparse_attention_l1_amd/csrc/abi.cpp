@@ -198,10 +198,11 @@ HSASTEP_API int hsa_kv_update(uint16_t* k_cache, uint16_t* v_cache, const uint16
                     "kv update");
 }
 
-HSASTEP_API int hsa_attention_active(const uint16_t* q_active, const uint16_t* k_cache,
-                                     const uint16_t* v_cache, uint16_t* out, int64_t n_active,
-                                     int64_t n_tokens, int32_t batch, int32_t heads,
-                                     int32_t head_dim, float softmax_scale, void* stream) {
+namespace {
+
+int check_attention(const uint16_t* q_active, const uint16_t* k_cache, const uint16_t* v_cache,
+                    uint16_t* out, int64_t n_active, int64_t n_tokens, int32_t batch,
+                    int32_t heads, int32_t head_dim, float softmax_scale) {
   if (n_tokens < 1 || n_tokens > INT32_MAX || n_active < 0 || n_active > INT32_MAX ||
       batch < 1 || heads < 1)
     return fail(HSASTEP_ERR_ARG, "need 1 <= n_tokens < 2^31, 0 <= n_active < 2^31, batch, "
@@ -218,8 +219,68 @@ HSASTEP_API int hsa_attention_active(const uint16_t* q_active, const uint16_t* k
   const int64_t qtiles = (n_active + 127) / 128;
   if (qtiles * heads * int64_t(batch) > INT32_MAX)
     return fail(HSASTEP_ERR_ARG, "grid too large");
+  return ok();
+}
+
+}  // namespace
+
+HSASTEP_API size_t hsastep_attention_workspace_bytes(int64_t n_active, int64_t n_tokens,
+                                                     int32_t batch, int32_t heads,
+                                                     int32_t head_dim) {
+  if (n_active < 1 || n_tokens < 1 || batch < 1 || heads < 1) return 0;
+  return hsastep::attention_split_workspace_bytes(n_active, n_tokens, batch, heads, head_dim);
+}
+
+HSASTEP_API int hsastep_attention_plan(int64_t n_active, int64_t n_tokens, int32_t batch,
+                                       int32_t heads, int32_t head_dim, int32_t compute_units,
+                                       size_t workspace_bytes, int32_t* plan_host) {
+  if (plan_host == nullptr) return fail(HSASTEP_ERR_ARG, "plan_host is null");
+  if (n_active < 1 || n_tokens < 1 || batch < 1 || heads < 1 || compute_units < 0)
+    return fail(HSASTEP_ERR_ARG, "need n_active, n_tokens, batch, heads >= 1, compute_units >= 0");
+  const int64_t tiles = (n_active + 255) / 256 * heads * int64_t(batch);
+  if (!hsastep::attention_pipe_fits(n_tokens, heads, head_dim) || tiles > INT32_MAX) {
+    plan_host[0] = plan_host[1] = plan_host[2] = plan_host[3] = 0;   // kernel without splits
+    return ok();
+  }
+  const hsastep::AttentionPlan p = hsastep::attention_plan(n_active, n_tokens, batch, heads,
+                                                           compute_units, workspace_bytes);
+  plan_host[0] = p.full_tiles;
+  plan_host[1] = p.splits > 1 ? p.tail_tiles : 0;
+  plan_host[2] = p.splits;
+  plan_host[3] = p.splits > 1 ? p.piece_keys : 0;
+  return ok();
+}
+
+HSASTEP_API int hsa_attention_active_ws(const uint16_t* q_active, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, uint16_t* out, int64_t n_active,
+                                        int64_t n_tokens, int32_t batch, int32_t heads,
+                                        int32_t head_dim, float softmax_scale, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (int rc = check_attention(q_active, k_cache, v_cache, out, n_active, n_tokens, batch, heads,
+                               head_dim, softmax_scale))
+    return rc;
+  if (n_active == 0) return ok();
+  if (workspace_bytes > 0 && workspace == nullptr)
+    return fail(HSASTEP_ERR_WORKSPACE, "workspace_bytes > 0 with a null workspace");
+  if (workspace != nullptr && !aligned16(workspace))
+    return fail(HSASTEP_ERR_ARG, "workspace must be 16-byte aligned");
   return hip_status(hsastep::launch_attention(q_active, k_cache, v_cache, out, n_active, n_tokens,
                                               batch, heads, head_dim, softmax_scale,
+                                              workspace_bytes ? workspace : nullptr,
+                                              workspace_bytes, as_stream(stream)),
+                    "attention");
+}
+
+HSASTEP_API int hsa_attention_active(const uint16_t* q_active, const uint16_t* k_cache,
+                                     const uint16_t* v_cache, uint16_t* out, int64_t n_active,
+                                     int64_t n_tokens, int32_t batch, int32_t heads,
+                                     int32_t head_dim, float softmax_scale, void* stream) {
+  if (int rc = check_attention(q_active, k_cache, v_cache, out, n_active, n_tokens, batch, heads,
+                               head_dim, softmax_scale))
+    return rc;
+  if (n_active == 0) return ok();
+  return hip_status(hsastep::launch_attention(q_active, k_cache, v_cache, out, n_active, n_tokens,
+                                              batch, heads, head_dim, softmax_scale, nullptr, 0,
                                               as_stream(stream)),
                     "attention");
 }

@@ -40,15 +40,28 @@ hipError_t launch_kv_update(uint16_t* k_cache, uint16_t* v_cache, const uint16_t
 // attn.hip: active-query full-context attention (bf16 MFMA, fp32 online softmax).
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
                             uint16_t* out, int64_t n_active, int64_t n_tokens, int batch, int heads,
-                            int head_dim, float softmax_scale, hipStream_t stream);
+                            int head_dim, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 // attn_pipe.hip: the head_dim 128 path of launch_attention (one wavefront per SIMD, 64
 // queries each, hand-scheduled key loop); fits() says whether a shape can take it.
 bool attention_pipe_fits(int64_t n_tokens, int heads, int head_dim);
+// With a workspace, the tiles of a last round that would leave compute units idle are split
+// into key ranges (pieces) whose partial results a merge kernel combines.
+constexpr int kMaxSplits = 8;       // key ranges per split tile
+constexpr int kMaxPieces = 512;     // pieces per launch (two rounds of 256 compute units)
+struct AttentionPlan {
+  int full_tiles, tail_tiles, splits, piece_keys;
+};
+AttentionPlan attention_plan(int64_t n_active, int64_t n_tokens, int batch, int heads, int cus,
+                             size_t workspace_bytes);
+size_t attention_piece_bytes();
+size_t attention_split_workspace_bytes(int64_t n_active, int64_t n_tokens, int batch, int heads,
+                                       int head_dim);
 hipError_t launch_attention_pipe(const uint16_t* q, const uint16_t* k_cache,
                                  const uint16_t* v_cache, uint16_t* out, int64_t n_active,
                                  int64_t n_tokens, int batch, int heads, float softmax_scale,
-                                 hipStream_t stream);
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 // proj.hip: fused QKV projection of the active rows; Q compacted, K/V into their cache slots.
 hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w, const uint16_t* bias,

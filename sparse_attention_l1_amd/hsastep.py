@@ -37,6 +37,10 @@ _SIGS = {
     "hsastep_gather_rows": ([_p, _p, _p, _i64, _i64, _i64, _p], ctypes.c_int),
     "hsa_kv_update": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p], ctypes.c_int),
     "hsa_attention_active": ([_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _f, _p], ctypes.c_int),
+    "hsastep_attention_workspace_bytes": ([_i64, _i64, _i32, _i32, _i32], _sz),
+    "hsastep_attention_plan": ([_i64, _i64, _i32, _i32, _i32, _i32, _sz, _p], ctypes.c_int),
+    "hsa_attention_active_ws": ([_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _f, _p, _sz, _p],
+                                ctypes.c_int),
     "hsa_euler_step": ([_p, _p, _p, _p, _i64, _i64, _i32, _f, _f, _p], ctypes.c_int),
     "hsa_qkv_project": ([_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p],
                         ctypes.c_int),
@@ -201,6 +205,41 @@ def hsa_attention_active(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                     _dev(v_cache, "v_cache", _BF16), _dev(out, "out", _BF16), A, N,
                                     B, H, D, float(softmax_scale), _stream(stream)),
            "hsa_attention_active")
+
+
+def hsastep_attention_workspace_bytes(n_active: int, n_tokens: int, batch: int, heads: int,
+                                      head_dim: int) -> int:
+    return int(lib.hsastep_attention_workspace_bytes(n_active, n_tokens, batch, heads, head_dim))
+
+
+def hsastep_attention_plan(n_active: int, n_tokens: int, batch: int, heads: int, head_dim: int,
+                           compute_units: int, workspace_bytes: int):
+    """(whole tiles, split tiles, key ranges per split tile, keys per range)."""
+    out = (ctypes.c_int32 * 4)()
+    _check(lib.hsastep_attention_plan(n_active, n_tokens, batch, heads, head_dim, compute_units,
+                                      workspace_bytes, out), "hsastep_attention_plan")
+    return tuple(out)
+
+
+def attention_workspace(n_active: int, n_tokens: int, batch: int, heads: int, head_dim: int,
+                        device="cuda") -> torch.Tensor:
+    n = hsastep_attention_workspace_bytes(n_active, n_tokens, batch, heads, head_dim)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def hsa_attention_active_ws(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            out: torch.Tensor, softmax_scale: float, ws: Optional[torch.Tensor],
+                            stream=None) -> None:
+    """hsa_attention_active with a workspace (ws=None runs it without one)."""
+    B, A, H, D = q.shape
+    Bk, N, Hk, Dk = k_cache.shape
+    if (Bk, Hk, Dk) != (B, H, D) or v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch")
+    _check(lib.hsa_attention_active_ws(
+        _dev(q, "q", _BF16), _dev(k_cache, "k_cache", _BF16), _dev(v_cache, "v_cache", _BF16),
+        _dev(out, "out", _BF16), A, N, B, H, D, float(softmax_scale),
+        None if ws is None else _dev(ws, "workspace", (torch.uint8,)),
+        0 if ws is None else ws.numel(), _stream(stream)), "hsa_attention_active_ws")
 
 
 def hsa_qkv_project(x_active: torch.Tensor, w_qkv: torch.Tensor, bias: Optional[torch.Tensor],

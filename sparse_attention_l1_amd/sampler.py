@@ -7,7 +7,7 @@ Staptoewijzing (HSA) voor Efficiënte Videogeneratie", §2.1-§2.4):
     active set A_i          hsa_active_set        (|A_i| known on the host, no sync)
     per layer:  model(A_i) -> q, k_new, v_new for the active tokens
                 hsa_kv_update         fresh K/V rows overwrite their cache slots
-                hsa_attention_active  active queries x all N cached rows
+                hsa_attention_active_ws  active queries x all N cached rows
     model(A_i) -> fresh velocities of the active tokens
     (at iteration max(m,1)-1, where every token is active; with reselect=True also
      at every later iteration in which every token is active)
@@ -57,6 +57,9 @@ class HsaSampler:
         self.v_cache: List[torch.Tensor] = [torch.empty(shape, dtype=torch.bfloat16, device=dev)
                                             for _ in range(layers)]
         self.attn_out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        # lets attention split the key range of a last round of query tiles that would leave
+        # compute units idle (iterations with few active tokens)
+        self.attn_ws = hs.attention_workspace(n_tokens, n_tokens, batch, heads, head_dim, dev)
         self.n_active = n_tokens
         self.selection_iter = max(m, 1) - 1
         self.reselect = reselect
@@ -85,7 +88,8 @@ class HsaSampler:
         na = self.n_active
         out = self.attn_out.view(-1)[: self.B * na * self.H * self.D].view(self.B, na, self.H, self.D)
         hs.hsa_kv_update(self.k_cache[l], self.v_cache[l], k_new, v_new, self.active_idx, na)
-        hs.hsa_attention_active(q, self.k_cache[l], self.v_cache[l], out, self.scale)
+        hs.hsa_attention_active_ws(q, self.k_cache[l], self.v_cache[l], out, self.scale,
+                                   self.attn_ws)
         return out
 
     def euler(self, i: int, v_fresh: torch.Tensor) -> None:

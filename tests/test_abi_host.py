@@ -181,3 +181,30 @@ def test_workspace_size_monotone(hs):
     b = hs.hsastep_workspace_bytes(100000, 4)
     assert 0 < a < b
     assert hs.hsastep_workspace_bytes(75600, 16) >= 75600 * 4 + 4 * (75600 // 1024)
+
+
+def test_attention_plan(hs):
+    """The split planner of hsa_attention_active_ws on a 256-CU device, for the workloads'
+    shapes: whole rounds are never split; a half-empty last round is split so that its work
+    spreads over the chip; the workspace bounds the plan."""
+    ws = lambda a, n, b, h: hs.hsastep_attention_workspace_bytes(a, n, b, h, 128)
+    plan = lambda a, n, b, h, w=None: hs.hsastep_attention_plan(
+        a, n, b, h, 128, 256, ws(a, n, b, h) if w is None else w)
+    assert plan(16380, 32760, 1, 12) == (768, 0, 1, 0)            # 3 whole rounds
+    assert plan(32760, 32760, 1, 12) == (1536, 0, 1, 0)           # 6 whole rounds
+    full, tail, s, keys = plan(8190, 32760, 1, 12)                 # 384 tiles = 1.5 rounds
+    assert (full, tail) == (256, 128) and s >= 2 and 128 * s <= 512
+    assert (s - 1) * keys < 32760 <= s * keys and keys % 32 == 0
+    full, tail, s, keys = plan(7560, 75600, 2, 40)                 # 2400 tiles = 9.4 rounds
+    assert (full, tail) == (2304, 96) and 96 * s <= 512 and s > 1
+    assert plan(300, 3000, 2, 3)[1:3] == (12, 8)                   # all tiles split, 8 ranges
+    assert plan(300, 3000, 2, 3, w=0) == (12, 0, 1, 0)             # no workspace: no split
+    piece = ws(300, 3000, 2, 3) // 96
+    assert plan(300, 3000, 2, 3, w=piece * 24)[1:3] == (12, 2)     # room for 24 pieces
+    assert plan(300, 3000, 2, 3, w=piece * 24)[3] == 1504
+    assert hs.hsastep_attention_plan(300, 3000, 2, 3, 64, 256, 10 ** 9) == (0, 0, 0, 0)
+    assert hs.hsastep_attention_plan(300, 200, 2, 3, 128, 256, 10 ** 9) == (0, 0, 0, 0)
+    for a, n in ((70, 1275), (513, 700), (1100, 20000)):
+        full, tail, s, keys = plan(a, n, 2, 40)
+        if s > 1:
+            assert n - (s - 1) * keys >= 256                       # every range >= 8 blocks
