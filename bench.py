@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of one HSA denoise iteration on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--loop] [--pair]
-                    [--sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-loop]
+                    [--no-streaming] [--pair] [--sweep] [--proj]
 
 A step is one pass of the whole path over the single-step workload (N = 32760
 tokens on a 21x30x52 latent grid, 12 heads x 128, 64 latent channels, half of
@@ -14,8 +14,10 @@ seeded synthetic data already resident in HBM.  Prints one JSON line.
 value = attention FLOPs of the iteration (4 * |A| * N * H * D) / wall time of the
 whole iteration, in TFLOP/s; ms_per_step is that wall time.  The roofline entry
 is the attention kernel alone, timed with HIP events around each launch.
-With --loop the full 40-iteration, 30-layer schedule (T=40, budgets {40,20,10,5},
-m=4) is also run once and its mean ms per iteration reported; --pair does the same for
+The full 40-iteration, 30-layer schedule (T=40, budgets {40,20,10,5}, m=4) is also run
+once and its mean ms per iteration reported (the metric's second half), as are the
+HBM-bound kernels one by one with their fraction of 8 TB/s and a plain-copy ceiling at the
+same sizes; --pair does the same for
 the aggressive cond/uncond pair (B=2, N=75600, 40x128 heads, 40 layers, T=40, budgets
 {40,10,5} over 10/30/60% of the tokens, m=2).
 """
@@ -50,7 +52,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
-    p.add_argument("--loop", action="store_true", help="also time the full 40-iteration schedule")
+    p.add_argument("--no-loop", action="store_true",
+                   help="skip the full 40-iteration, 30-layer schedule (run by default)")
+    p.add_argument("--no-streaming", action="store_true",
+                   help="skip the per-kernel HBM figures and the copy ceiling (run by default)")
     p.add_argument("--pair", action="store_true",
                    help="also run the aggressive cond/uncond pair: B=2, N=75600, 40x128 heads, "
                         "40 layers, T=40 {40,10,5} over 10/30/60%%, m=2 (~2-3 minutes, 124 GB "
@@ -137,6 +142,7 @@ class SingleStep:
         self.x_act = torch.empty((na, C), dtype=torch.float32, device=dev)
         self.v_fresh = torch.empty((na, C), dtype=torch.float32, device=dev)
         self.ws = hs.workspace(N, cfg.n_groups, dev)
+        self.attn_ws = hs.attention_workspace(na, N, cfg.batch, H, D, dev)
         sig = np.linspace(1.0, 0.0, cfg.T + 1, dtype=np.float64).astype(np.float32)
         self.s_cur, self.s_next = float(sig[cfg.iteration]), float(sig[cfg.iteration + 1])
         self.scale = float(np.float32(1.0 / np.sqrt(D)))
@@ -152,11 +158,126 @@ class SingleStep:
         hs.hsa_kv_update(self.k_cache, self.v_cache, self.k_new, self.v_new, self.active_idx, na)
         if ev is not None:
             ev[0].record()
-        hs.hsa_attention_active(self.q, self.k_cache, self.v_cache, self.out, self.scale)
+        hs.hsa_attention_active_ws(self.q, self.k_cache, self.v_cache, self.out, self.scale,
+                                   self.attn_ws)
         if ev is not None:
             ev[1].record()
         hs.hsa_euler_step(self.x, self.v_hat, self.v_fresh, self.active_pos, na, self.s_cur,
                           self.s_next)
+
+
+def _event_ms(torch, fn, reps, flush=None):
+    """Mean GPU ms per call, from an event pair around each call.  Warm: the calls queue
+    behind a ~2 ms spin of the GPU, so the host enqueues them all before the GPU reaches them
+    and the gap between consecutive calls is the GPU's own; the data stays in the caches.
+    Cold: each call runs after a read of a 1 GiB buffer, which evicts the 256 MB infinity
+    cache with clean lines, so its inputs come from HBM."""
+    fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    if flush is None:
+        torch.cuda._sleep(4_000_000)
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def run_streaming(hs, synth, torch, st, reps=20):
+    """The HBM-bound steps one by one: per call, microseconds, algorithmic bytes and the
+    fraction of 8 TB/s, at the single-step sizes (warm: back-to-back calls, the figure the
+    kernel trace of the single-step sequence gives) and from HBM (cold); Euler and the score
+    also at the large-head sweep size (N = 75600, from HBM); and the floor of a launch that
+    moves 16 bytes.  The selection and the active set are latency bound (several dependent
+    launches over 4N-byte arrays) and are reported in microseconds."""
+    dev = torch.device("cuda")
+    c = st.cfg
+    N, C, H, D, na = c.n_tokens, c.channels, c.heads, c.head_dim, st.na
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
+    flush = lambda: torch.sum(flush_buf, dim=0, keepdim=True, out=flush_out)
+    one_idx = torch.zeros(1, dtype=torch.int32, device=dev)
+    tiny_src = torch.zeros((1, 4), dtype=torch.float32, device=dev)
+    tiny_dst = torch.empty_like(tiny_src)
+    out = {"peak_gbs": PEAK_HBM_GBS, "kernels": {}}
+
+    def entry(name, fn, nbytes, cold=True):
+        e = {"us_warm": _event_ms(torch, fn, reps) * 1e3}
+        if cold:
+            e["us_cold"] = _event_ms(torch, fn, max(reps // 2, 5), flush) * 1e3
+        if nbytes:
+            e["bytes"] = nbytes
+            for k in ("warm", "cold"):
+                if f"us_{k}" in e:
+                    e[f"gbs_{k}"] = nbytes / e[f"us_{k}"] / 1e3
+                    e[f"frac_{k}"] = e[f"gbs_{k}"] / PEAK_HBM_GBS
+        out["kernels"][name] = e
+
+    entry("launch_floor (gather of one 16-byte row)",
+          lambda: hs.hsastep_gather_rows(tiny_dst, tiny_src, one_idx, 1), 0)
+    entry("kv_update", lambda: hs.hsa_kv_update(st.k_cache, st.v_cache, st.k_new, st.v_new,
+                                                st.active_idx, na),
+          4.0 * c.batch * na * H * D * 2 + 4 * na)
+    entry("gather_rows (active latent rows)",
+          lambda: hs.hsastep_gather_rows(st.x_act, st.x, st.active_idx, na), 2.0 * na * C * 4 + 4 * na)
+    entry("euler_step", lambda: hs.hsa_euler_step(st.x, st.v_hat, st.v_fresh, st.active_pos, na,
+                                                  st.s_cur, st.s_next),
+          3.0 * N * C * 4 + na * C * 4 + 4 * N)
+    entry("select_groups (score + 4 grouping launches)",
+          lambda: hs.hsa_select_groups(st.v_prev, st.v_cur, c.sizes, st.group_id, None, st.ws),
+          2.0 * N * C * 4 + 4 * N)
+    entry("active_set (2 launches)",
+          lambda: hs.hsa_active_set(st.group_id, c.budgets, c.sizes, c.T, c.m, c.iteration,
+                                    st.active_idx, st.active_pos, st.ws), 0)
+    # the large-head sweep's latent (N = 75600, 64 channels, half the tokens active), from HBM
+    N4 = 75600
+    g = torch.Generator(device=dev).manual_seed(20260512)
+    x4 = torch.randn((N4, C), device=dev, generator=g)
+    vh4 = torch.randn((N4, C), device=dev, generator=g)
+    vc4 = torch.randn((N4, C), device=dev, generator=g)
+    na4 = N4 // 2
+    pos4 = torch.full((N4,), -1, dtype=torch.int32, device=dev)
+    pos4[::2] = torch.arange(na4, dtype=torch.int32, device=dev)
+    vf4 = torch.randn((na4, C), device=dev, generator=g)
+    g4 = torch.empty(N4, dtype=torch.int32, device=dev)
+    ws4 = hs.workspace(N4, 1, dev)
+    entry("euler_step N=75600", lambda: hs.hsa_euler_step(x4, vh4, vf4, pos4, na4, 0.875, 0.85),
+          3.0 * N4 * C * 4 + na4 * C * 4 + 4 * N4)
+    entry("select_groups K=1 N=75600 (score + assignment)",
+          lambda: hs.hsa_select_groups(vh4, vc4, (N4,), g4, None, ws4), 2.0 * N4 * C * 4 + 4 * N4)
+    # plain device copy (torch copy_) moving the same byte counts, and 1 GiB: the ceiling a
+    # streaming kernel of that size can reach
+    copies = {}
+    for moved in (16.9e6, 29.5e6, 68.0e6, 201.3e6, 2 ** 31):
+        n = int(moved / 8)
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        us_w = _event_ms(torch, lambda: b.copy_(a), reps) * 1e3
+        us_c = _event_ms(torch, lambda: b.copy_(a), 5, flush) * 1e3
+        copies[f"{moved / 1e6:.1f} MB"] = {"us_warm": us_w, "us_cold": us_c,
+                                           "gbs_warm": 8.0 * n / us_w / 1e3,
+                                           "gbs_cold": 8.0 * n / us_c / 1e3}
+        del a, b
+    out["copy_ceiling"] = copies
+    # the library's own row copy (hsastep_gather_rows with the identity index, 256-byte rows)
+    own = {}
+    for moved in (29.5e6, 68.0e6, 201.3e6, 2 ** 31):
+        rows = int(moved / 2 / 256)
+        a = torch.ones((rows, 64), dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        idx = torch.arange(rows, dtype=torch.int32, device=dev)
+        fn = lambda: hs.hsastep_gather_rows(b, a, idx, rows)
+        us_c = _event_ms(torch, fn, 5, flush) * 1e3
+        own[f"{moved / 1e6:.1f} MB"] = {"us_cold": us_c, "gbs_cold": 2.0 * rows * 256 / us_c / 1e3}
+        del a, b, idx
+    out["row_copy_ceiling"] = own
+    del flush_buf
+    return out
 
 
 def cpu_baseline(budget_s: float):
@@ -386,7 +507,8 @@ def run_sweep(hs, synth, torch, reps=5):
         vf = torch.empty((na, C), dtype=torch.float32, device=dev)
         hs.hsastep_gather_rows(vf, vcur, idx, na)
         flops = 4.0 * na * N * H * D
-        t_att = timed(lambda: hs.hsa_attention_active(q, kc, vc, o, scale))
+        aws = hs.attention_workspace(na, N, 1, H, D, dev)
+        t_att = timed(lambda: hs.hsa_attention_active_ws(q, kc, vc, o, scale, aws))
         t_sel = timed(lambda: hs.hsa_select_groups(vp, vcur, cfg.sizes, g, None, ws))
         t_act = timed(lambda: hs.hsa_active_set(g, cfg.budgets, cfg.sizes, cfg.T, cfg.m,
                                                 cfg.iteration, idx, pos, ws))
@@ -462,7 +584,10 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
     }
-    if args.loop:
+    if not args.no_streaming:
+        print("bench: streaming kernels and copy ceiling", file=sys.stderr, flush=True)
+        res["streaming_kernels"] = run_streaming(hs, synth, torch, st)
+    if not args.no_loop:
         print("bench: full schedule loop", file=sys.stderr, flush=True)
         res["full_schedule"] = run_loop(hs, synth, torch, synth.full_schedule())
     if args.pair:
