@@ -7,7 +7,7 @@
 A step is one pass of the whole path over the single-step workload (N = 32760
 tokens on a 21x30x52 latent grid, 12 heads x 128, 64 latent channels, half of
 the tokens active): token selection by L1 relative velocity change, the active
-set, the gather of the active rows, the KV-cache scatter, active-query
+set with the gather of the active latent rows, the KV-cache scatter, active-query
 attention against all N cached rows, and the cached Euler update.  Inputs are
 seeded synthetic data already resident in HBM.  Prints one JSON line.
 
@@ -139,7 +139,7 @@ class SingleStep:
         self.group_id = torch.empty(N, dtype=torch.int32, device=dev)
         self.active_idx = torch.empty(N, dtype=torch.int32, device=dev)
         self.active_pos = torch.empty(N, dtype=torch.int32, device=dev)
-        self.x_act = torch.empty((na, C), dtype=torch.float32, device=dev)
+        self.x_act = torch.empty((N, C), dtype=torch.float32, device=dev)
         self.v_fresh = torch.empty((na, C), dtype=torch.float32, device=dev)
         self.ws = hs.workspace(N, cfg.n_groups, dev)
         self.attn_ws = hs.attention_workspace(na, N, cfg.batch, H, D, dev)
@@ -151,9 +151,10 @@ class SingleStep:
     def step(self, ev=None):
         hs, c = self.hs, self.cfg
         hs.hsa_select_groups(self.v_prev, self.v_cur, c.sizes, self.group_id, None, self.ws)
-        na = hs.hsa_active_set(self.group_id, c.budgets, c.sizes, c.T, c.m, c.iteration,
-                               self.active_idx, self.active_pos, self.ws)
-        hs.hsastep_gather_rows(self.x_act, self.x, self.active_idx, na)      # model input rows
+        # the active set and the model's input rows (the active tokens' latent rows)
+        na = hs.hsa_active_set_gather(self.group_id, c.budgets, c.sizes, c.T, c.m, c.iteration,
+                                      self.active_idx, self.active_pos, self.x, self.x_act,
+                                      self.ws)
         hs.hsastep_gather_rows(self.v_fresh, self.v_model, self.active_idx, na)  # model stand-in
         hs.hsa_kv_update(self.k_cache, self.v_cache, self.k_new, self.v_new, self.active_idx, na)
         if ev is not None:
@@ -231,6 +232,10 @@ def run_streaming(hs, synth, torch, st, reps=20):
     entry("select_groups (score + 4 grouping launches)",
           lambda: hs.hsa_select_groups(st.v_prev, st.v_cur, c.sizes, st.group_id, None, st.ws),
           2.0 * N * C * 4 + 4 * N)
+    entry("active_set_gather (2 launches, with the active latent rows)",
+          lambda: hs.hsa_active_set_gather(st.group_id, c.budgets, c.sizes, c.T, c.m, c.iteration,
+                                           st.active_idx, st.active_pos, st.x, st.x_act, st.ws),
+          2.0 * na * C * 4 + 8.0 * N + 4 * na)
     entry("active_set (2 launches)",
           lambda: hs.hsa_active_set(st.group_id, c.budgets, c.sizes, c.T, c.m, c.iteration,
                                     st.active_idx, st.active_pos, st.ws), 0)

@@ -125,6 +125,24 @@ int hsa_active_set(const int32_t* group_id, int64_t n_tokens, const int32_t* bud
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hsa_active_set fused with the gather of the active tokens' rows of one per-token array
+ * ([HSA-nl] §2.2 item 1: only the active tokens enter the model; their latent rows are the
+ * model's input), in the same two launches: same arguments, result, validation and errors
+ * as hsa_active_set, plus
+ *
+ *   rows               [n_tokens, row_bytes] device array (e.g. the latent, fp32 [N, C])
+ *   row_bytes          a positive multiple of 4 (16 and 16-byte aligned pointers take the
+ *                      vector path)
+ *   rows_out           [n_tokens, row_bytes] output: rows_out[a] = rows[active_idx[a]] for
+ *                      a < |A_i|; rows past |A_i| are not written.  Must not alias rows.
+ */
+int hsa_active_set_gather(const int32_t* group_id, int64_t n_tokens, const int32_t* budgets_host,
+                          const int64_t* group_sizes_host, int32_t n_groups, int32_t T, int32_t m,
+                          int32_t iter, int32_t* active_idx, int32_t* active_pos,
+                          int64_t* n_active_host, const void* rows, int64_t row_bytes,
+                          void* rows_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * hsa_active_set without a workspace, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
  * arguments, result, validation and errors as hsa_active_set, minus the workspace.  The

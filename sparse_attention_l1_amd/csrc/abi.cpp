@@ -137,6 +137,36 @@ HSASTEP_API int hsa_active_set(const int32_t* group_id, int64_t n_tokens,
                     "active set");
 }
 
+HSASTEP_API int hsa_active_set_gather(const int32_t* group_id, int64_t n_tokens,
+                                      const int32_t* budgets_host,
+                                      const int64_t* group_sizes_host, int32_t n_groups,
+                                      int32_t T, int32_t m, int32_t iter, int32_t* active_idx,
+                                      int32_t* active_pos, int64_t* n_active_host,
+                                      const void* rows, int64_t row_bytes, void* rows_out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  std::string msg;
+  if (hsastep::check_schedule(n_tokens, budgets_host, group_sizes_host, n_groups, T, m, msg))
+    return fail(HSASTEP_ERR_ARG, msg);
+  if (iter < 0 || iter >= T) return fail(HSASTEP_ERR_ARG, "iter must be in [0, T)");
+  if (!group_id || !active_idx || !active_pos || !n_active_host || !rows || !rows_out)
+    return fail(HSASTEP_ERR_ARG, "null pointer argument");
+  if (row_bytes < 4 || row_bytes % 4 != 0)
+    return fail(HSASTEP_ERR_ARG, "row_bytes must be a positive multiple of 4");
+  if ((reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(rows_out)) & 3u)
+    return fail(HSASTEP_ERR_ARG, "rows / rows_out must be 4-byte aligned");
+  const hsastep::WorkspaceLayout wl = hsastep::workspace_layout(n_tokens, n_groups);
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(HSASTEP_ERR_WORKSPACE, "workspace smaller than hsastep_workspace_bytes()");
+  const uint32_t mask = hsastep::group_active_mask(budgets_host, n_groups, T, m, iter);
+  *n_active_host = hsastep::n_active_from_mask(mask, group_sizes_host, n_groups);
+  int32_t* blockcnt =
+      reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.blockcnt_off);
+  return hip_status(hsastep::launch_active(group_id, n_tokens, mask, n_groups, active_idx,
+                                           active_pos, blockcnt, as_stream(stream), rows,
+                                           row_bytes, rows_out),
+                    "active set + gather");
+}
+
 HSASTEP_API int hsa_active_set_noalloc(const int32_t* group_id, int64_t n_tokens,
                                        const int32_t* budgets_host,
                                        const int64_t* group_sizes_host, int32_t n_groups,

@@ -7,10 +7,14 @@
 // Compaction keeps ascending token order (the cache slots of the active rows):
 //   count kernel:   workgroup b counts the active tokens of its 1024-token chunk
 //   compact kernel: workgroup b adds the counts of chunks < b, scans its own
-//                   chunk with wavefront ballots, writes active_idx and active_pos.
+//                   chunk with wavefront ballots, writes active_idx and active_pos, and
+//                   (hsa_active_set_gather) copies the chunk's active rows of a per-token
+//                   array into active order ([HSA-nl] §2.2 item 1: only the active tokens
+//                   enter the model).
 // Two launches instead of one chained scan: no workgroup ever waits on another.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "host.hpp"
@@ -56,13 +60,27 @@ __global__ __launch_bounds__(kThreads) void active_count_kernel(const int32_t* _
   }
 }
 
+// Optional fused row gather: rows_out[a] = rows[active_idx[a]], rows of `words` units of Vec.
+template <typename Vec>
+struct RowGather {
+  const Vec* rows;
+  Vec* rows_out;
+  int64_t words;
+};
+
+template <typename Vec, bool kGather>
 __global__ __launch_bounds__(kThreads) void active_compact_kernel(
     const int32_t* __restrict__ gid, int64_t n_tokens, uint32_t mask, int n_groups,
     const int32_t* __restrict__ blockcnt, int32_t* __restrict__ active_idx,
-    int32_t* __restrict__ active_pos) {
+    int32_t* __restrict__ active_pos, RowGather<Vec> rg) {
   __shared__ int64_t part[kWaves];
   __shared__ int wsum[kWaves];
+  __shared__ int32_t s_tok[kGather ? kActiveBlockTokens : 1];   // this chunk's active tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // with the row gather, gridDim.y workgroups share a chunk: each repeats the chunk's scan
+  // (4 KB of group ids), the first writes the index lists, and each copies its share of the
+  // chunk's rows, so that the copy runs on many more compute units than there are chunks
+  const bool lists = blockIdx.y == 0;
 
   // offset of this chunk = active tokens in all earlier chunks
   int64_t acc = 0;
@@ -88,17 +106,40 @@ __global__ __launch_bounds__(kThreads) void active_compact_kernel(
     base += part[w];
     if (w < wave) base += wsum[w];
   }
+  int64_t chunk_first = 0;                     // active tokens in all earlier chunks
+  int count = 0;                               // active tokens in this chunk
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    chunk_first += part[w];
+    count += wsum[w];
+  }
   int64_t pos = base + (incl - mine);
+  int local = int(pos - chunk_first);          // position inside the chunk
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int64_t n = first + j;
     if (n >= n_tokens) break;
     if ((flags >> j) & 1) {
-      active_idx[pos] = int32_t(n);
-      active_pos[n] = int32_t(pos);
+      if (lists) {
+        active_idx[pos] = int32_t(n);
+        active_pos[n] = int32_t(pos);
+      }
+      if (kGather) s_tok[local++] = int32_t(n);
       ++pos;
-    } else {
+    } else if (lists) {
       active_pos[n] = -1;
+    }
+  }
+  if (kGather) {
+    // the chunk's active rows, in active order, from LDS: consecutive threads move
+    // consecutive units of a row, so each row is one coalesced segment on both sides
+    __syncthreads();
+    const int r0 = int(int64_t(count) * blockIdx.y / gridDim.y);
+    const int r1 = int(int64_t(count) * (blockIdx.y + 1) / gridDim.y);
+    const int64_t total = int64_t(r1 - r0) * rg.words;
+    for (int64_t t = tid; t < total; t += kThreads) {
+      const int64_t r = r0 + t / rg.words, c = t % rg.words;
+      rg.rows_out[(chunk_first + r) * rg.words + c] = rg.rows[int64_t(s_tok[r]) * rg.words + c];
     }
   }
 }
@@ -134,14 +175,32 @@ hipError_t active_scratch(int32_t** ptr) {
 
 hipError_t launch_active(const int32_t* group_id, int64_t n_tokens, uint32_t group_mask,
                          int n_groups, int32_t* active_idx, int32_t* active_pos, int32_t* blockcnt,
-                         hipStream_t stream) {
+                         hipStream_t stream, const void* rows, int64_t row_bytes,
+                         void* rows_out) {
   const int64_t nblk = (n_tokens + kActiveBlockTokens - 1) / kActiveBlockTokens;
   active_count_kernel<<<dim3(unsigned(nblk)), dim3(kThreads), 0, stream>>>(
       group_id, n_tokens, group_mask, n_groups, blockcnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  active_compact_kernel<<<dim3(unsigned(nblk)), dim3(kThreads), 0, stream>>>(
-      group_id, n_tokens, group_mask, n_groups, blockcnt, active_idx, active_pos);
+  // gather: about 1024 workgroups in all (4 per compute unit), at most 16 per chunk
+  const int64_t share = rows ? std::min<int64_t>(16, std::max<int64_t>(1, 1024 / nblk)) : 1;
+  const dim3 grid{unsigned(nblk), unsigned(share)}, block{unsigned(kThreads)};
+  const uintptr_t al = reinterpret_cast<uintptr_t>(rows) | reinterpret_cast<uintptr_t>(rows_out);
+  if (rows == nullptr) {
+    active_compact_kernel<uint32_t, false><<<grid, block, 0, stream>>>(
+        group_id, n_tokens, group_mask, n_groups, blockcnt, active_idx, active_pos,
+        RowGather<uint32_t>{nullptr, nullptr, 0});
+  } else if (row_bytes % 16 == 0 && (al & 15u) == 0) {
+    active_compact_kernel<uint4, true><<<grid, block, 0, stream>>>(
+        group_id, n_tokens, group_mask, n_groups, blockcnt, active_idx, active_pos,
+        RowGather<uint4>{static_cast<const uint4*>(rows), static_cast<uint4*>(rows_out),
+                         row_bytes / 16});
+  } else {
+    active_compact_kernel<uint32_t, true><<<grid, block, 0, stream>>>(
+        group_id, n_tokens, group_mask, n_groups, blockcnt, active_idx, active_pos,
+        RowGather<uint32_t>{static_cast<const uint32_t*>(rows), static_cast<uint32_t*>(rows_out),
+                            row_bytes / 4});
+  }
   return hipGetLastError();
 }
 

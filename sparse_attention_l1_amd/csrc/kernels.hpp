@@ -19,10 +19,12 @@ hipError_t launch_score(const float* v_prev, const float* v_cur, int64_t n_token
 hipError_t launch_rank(const float* r, int64_t n_tokens, const int64_t* targets, int n_targets,
                        uint32_t* rank_ws, int32_t* group_id, hipStream_t stream);
 
-// active.hip: ascending active index list + inverse map for one iteration.
+// active.hip: ascending active index list + inverse map for one iteration; with rows, also
+// rows_out[a] = rows[active_idx[a]] (rows of row_bytes, a multiple of 4) in the same launch.
 hipError_t launch_active(const int32_t* group_id, int64_t n_tokens, uint32_t group_mask,
                          int n_groups, int32_t* active_idx, int32_t* active_pos, int32_t* blockcnt,
-                         hipStream_t stream);
+                         hipStream_t stream, const void* rows = nullptr, int64_t row_bytes = 0,
+                         void* rows_out = nullptr);
 
 // active.hip: device address of the library's own per-chunk count array on the current device
 // (kNoAllocMaxTokens / 1024 + 1 words), looked up once per device; for callers that cannot

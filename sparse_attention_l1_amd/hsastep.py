@@ -32,6 +32,8 @@ _SIGS = {
     "hsa_select_groups": ([_p, _p, _i64, _i32, _p, _i32, _p, _p, _p, _sz, _p], ctypes.c_int),
     "hsa_active_set": ([_p, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p],
                        ctypes.c_int),
+    "hsa_active_set_gather": ([_p, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _i64,
+                               _p, _p, _sz, _p], ctypes.c_int),
     "hsa_active_set_noalloc": ([_p, _i64, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p],
                                ctypes.c_int),
     "hsastep_gather_rows": ([_p, _p, _p, _i64, _i64, _i64, _p], ctypes.c_int),
@@ -144,6 +146,31 @@ def hsa_active_set(group_id: torch.Tensor, budgets: Sequence[int], group_sizes: 
         len(budgets), T, m, iteration, _dev(active_idx, "active_idx", (torch.int32,)),
         _dev(active_pos, "active_pos", (torch.int32,)), ctypes.byref(out),
         _dev(ws, "workspace", (torch.uint8,)), ws.numel(), _stream(stream)), "hsa_active_set")
+    return out.value
+
+
+def hsa_active_set_gather(group_id: torch.Tensor, budgets: Sequence[int],
+                          group_sizes: Sequence[int], T: int, m: int, iteration: int,
+                          active_idx: torch.Tensor, active_pos: torch.Tensor, rows: torch.Tensor,
+                          rows_out: torch.Tensor, ws: torch.Tensor, stream=None) -> int:
+    """hsa_active_set plus rows_out[a] = rows[active_idx[a]] for the active tokens (rows and
+    rows_out: [n_tokens, ...] with the same row size)."""
+    n = group_id.shape[0]
+    if active_idx.shape != (n,) or active_pos.shape != (n,):
+        raise ValueError("active_idx and active_pos must have n_tokens entries")
+    if rows.shape[0] != n or rows_out.shape[0] < n or rows_out.dtype != rows.dtype or \
+            rows_out[0].numel() != rows[0].numel():
+        raise ValueError("rows and rows_out must hold n_tokens rows of the same size")
+    row_bytes = rows[0].numel() * rows.element_size()
+    out = ctypes.c_int64(0)
+    anyt = (rows.dtype,)
+    _check(lib.hsa_active_set_gather(
+        _dev(group_id, "group_id", (torch.int32,)), n, _host_i32(budgets), _host_i64(group_sizes),
+        len(budgets), T, m, iteration, _dev(active_idx, "active_idx", (torch.int32,)),
+        _dev(active_pos, "active_pos", (torch.int32,)), ctypes.byref(out),
+        _dev(rows, "rows", anyt), row_bytes, _dev(rows_out, "rows_out", anyt),
+        _dev(ws, "workspace", (torch.uint8,)), ws.numel(), _stream(stream)),
+        "hsa_active_set_gather")
     return out.value
 
 

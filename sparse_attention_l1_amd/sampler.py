@@ -4,7 +4,8 @@ One call of ``HsaSampler.iteration(i, model)`` is one denoise iteration of
 Heterogeneous Step Allocation ("Technische Samenvatting: Heterogene
 Staptoewijzing (HSA) voor Efficiënte Videogeneratie", §2.1-§2.4):
 
-    active set A_i          hsa_active_set        (|A_i| known on the host, no sync)
+    active set A_i          hsa_active_set_gather (|A_i| known on the host, no sync; the
+                                                   active latent rows into x_active)
     per layer:  model(A_i) -> q, k_new, v_new for the active tokens
                 hsa_kv_update         fresh K/V rows overwrite their cache slots
                 hsa_attention_active_ws  active queries x all N cached rows
@@ -49,6 +50,8 @@ class HsaSampler:
         self.group_id = torch.zeros(n_tokens, dtype=torch.int32, device=dev)
         self.score = torch.empty(n_tokens, dtype=torch.float32, device=dev)
         self.active_idx = torch.empty(n_tokens, dtype=torch.int32, device=dev)
+        # the active tokens' latent rows in active order: the model's input at this iteration
+        self.x_active = torch.empty_like(self.x)
         self.active_pos = torch.empty(n_tokens, dtype=torch.int32, device=dev)
         self.ws = hs.workspace(n_tokens, len(budgets), dev)
         shape = (batch, n_tokens, heads, head_dim)
@@ -79,8 +82,9 @@ class HsaSampler:
         hs.hsa_select_groups(v_prev, v_cur, self.sizes, self.group_id, self.score, self.ws)
 
     def active_set(self, i: int) -> int:
-        self.n_active = hs.hsa_active_set(self.group_id, self.budgets, self.sizes, self.T, self.m, i,
-                                          self.active_idx, self.active_pos, self.ws)
+        self.n_active = hs.hsa_active_set_gather(self.group_id, self.budgets, self.sizes, self.T,
+                                                 self.m, i, self.active_idx, self.active_pos,
+                                                 self.x, self.x_active, self.ws)
         return self.n_active
 
     def attention_layer(self, l: int, q: torch.Tensor, k_new: torch.Tensor,

@@ -105,6 +105,21 @@ def test_active_set_rejects(hs):
     assert b"divide" in hs.lib.hsastep_last_error()
 
 
+def test_active_set_gather_rejects_on_the_host(hs):
+    b = (ctypes.c_int32 * 2)(40, 20)
+    sz = (ctypes.c_int64 * 2)(5, 5)
+    out = ctypes.c_int64(-7)
+    w = hs.hsastep_workspace_bytes(10, 2)
+    run = lambda rows, rb, rows_out, ws=w: call(hs, "hsa_active_set_gather", FAKE, 10, b, sz, 2,
+                                                40, 4, 5, FAKE, FAKE, ctypes.byref(out), rows, rb,
+                                                rows_out, FAKE, ws, None)
+    assert run(FAKE, 6, FAKE) == hs.ERR_ARG                      # row_bytes not a multiple of 4
+    assert run(FAKE, 0, FAKE) == hs.ERR_ARG
+    assert run(None, 16, FAKE) == hs.ERR_ARG
+    assert run(FAKE, 16, ctypes.c_void_p((1 << 20) + 2)) == hs.ERR_ARG   # misaligned
+    assert run(FAKE, 16, FAKE, ws=8) == hs.ERR_WORKSPACE
+
+
 def test_active_set_noalloc_rejects_on_the_host(hs):
     """Validation of the allocation-free variant runs before it looks up its scratch array
     or enqueues anything: schedule errors, more tokens than the array covers, null pointers."""

@@ -254,10 +254,14 @@ def run_loop_both(cfg, hs, layers=None, reselect=False):
         smp.select(dev(model.vm.v_prev), dev(model.vm(0)))
     for i in range(cfg.T):
         outs = {}
+        x_before = host(smp.x)
         smp.iteration(i, model, on_attention=lambda l, o: outs.__setitem__(l, host_bits(o)))
         torch.cuda.synchronize()
         want = rec[i]
         na = smp.n_active
+        # the model's input rows gathered with the active set
+        assert np.array_equal(host(smp.x_active)[:na].view(np.uint32),
+                              x_before[want["active_idx"]].view(np.uint32)), f"iteration {i}"
         assert na == want["active_idx"].shape[0], f"iteration {i}"
         assert np.array_equal(host(smp.active_idx)[:na], want["active_idx"]), f"iteration {i}"
         assert np.array_equal(host(smp.active_pos), want["active_pos"]), f"iteration {i}"
@@ -412,3 +416,31 @@ def test_aggressive_pair_full_size_loop(hs):
     q = model.src.rows("q", 0, check_i, na)[:, qrows]
     want = oracle.attention_active(q, caches["k"], caches["v"], scale)
     attn_close(got["attn"], want, f"pair loop i{check_i} sampled rows")
+
+
+# ----------------------------------------------------------------------------- active set + gather
+
+@pytest.mark.parametrize("N,row_words,budgets,sizes,T,m,it", [
+    (32760, 64, (40, 20), (16380, 16380), 40, 4, 5),          # fp32 latent rows, vector path
+    (1000, 3, (8, 4), (300, 700), 8, 1, 3),                   # 12-byte rows, word path
+    (5000, 65, (12, 6, 3), (1000, 1500, 2500), 12, 0, 4),    # 260-byte rows
+    (3000, 16, (8, 4), (0, 3000), 8, 1, 3),                   # no active token at all
+])
+def test_active_set_gather(hs, N, row_words, budgets, sizes, T, m, it):
+    rng = np.random.default_rng(N + row_words)
+    g_host = rng.permutation(np.repeat(np.arange(len(sizes)), sizes)).astype(np.int32)
+    rows = rng.standard_normal((N, row_words)).astype(np.float32)
+    g = dev(g_host)
+    idx = torch.full((N,), -9, dtype=torch.int32, device="cuda")
+    pos = torch.empty(N, dtype=torch.int32, device="cuda")
+    out = torch.full((N + 1, row_words), 7.0, dtype=torch.float32, device="cuda")
+    na = hs.hsa_active_set_gather(g, budgets, sizes, T, m, it, idx, pos, dev(rows), out,
+                                  hs.workspace(N, len(budgets)))
+    torch.cuda.synchronize()
+    want_idx, want_pos = oracle.active_set(g_host, budgets, T, m, it)
+    assert na == want_idx.shape[0]
+    assert np.array_equal(host(idx)[:na], want_idx) and np.all(host(idx)[na:] == -9)
+    assert np.array_equal(host(pos), want_pos)
+    got = host(out)
+    assert np.array_equal(got[:na].view(np.uint32), rows[want_idx].view(np.uint32))
+    assert np.all(got[na:] == 7.0)                 # nothing written past |A_i|
