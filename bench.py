@@ -448,6 +448,38 @@ def run_proj(hs, torch, reps=10):
     return out
 
 
+def run_split_gain(hs, torch, reps=5):
+    """Attention with and without the workspace in the same run, for the shapes whose last
+    round of query tiles leaves compute units idle: the full schedule at 25% and 75% active,
+    the aggressive pair at 10%, the sweep at f = 1 and 1/4 (seeded N(0,1) data, one layer)."""
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"compute_units": cus, "points": []}
+    gen = torch.Generator(device=dev).manual_seed(20260512)
+    for name, B, A, N, H in (("full schedule, 25% active", 1, 8190, 32760, 12),
+                             ("full schedule, 75% active", 1, 24570, 32760, 12),
+                             ("aggressive pair, 10% active", 2, 7560, 75600, 40),
+                             ("large-head sweep f=1", 1, 75600, 75600, 40),
+                             ("large-head sweep f=1/4", 1, 18900, 75600, 40)):
+        q = torch.randn((B, A, H, 128), device=dev, generator=gen).to(torch.bfloat16)
+        kc = torch.randn((B, N, H, 128), device=dev, generator=gen).to(torch.bfloat16)
+        vc = torch.randn((B, N, H, 128), device=dev, generator=gen).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        ws = hs.attention_workspace(A, N, B, H, 128, dev)
+        scale = float(np.float32(1.0 / np.sqrt(128)))
+        flops = 4.0 * B * A * N * H * 128
+        t_plain = _event_ms(torch, lambda: hs.hsa_attention_active(q, kc, vc, o, scale), reps)
+        t_ws = _event_ms(torch, lambda: hs.hsa_attention_active_ws(q, kc, vc, o, scale, ws), reps)
+        out["points"].append({
+            "shape": name, "batch": B, "n_active": A, "n_tokens": N, "heads": H,
+            "plan": list(hs.hsastep_attention_plan(A, N, B, H, 128, cus, ws.numel())),
+            "ms_without_workspace": t_plain, "ms_with_workspace": t_ws,
+            "tflops_without": flops / t_plain / 1e9, "tflops_with": flops / t_ws / 1e9})
+        print(f"bench: split {name}: {t_plain:.3f} -> {t_ws:.3f} ms", file=sys.stderr, flush=True)
+        del q, kc, vc, o, ws
+    return out
+
+
 def run_sweep(hs, synth, torch, reps=5):
     """Large-head sweep (N=75600 on a 21x45x80 grid, 40 heads x 128, 64 channels): per active
     fraction f, each kernel of one iteration timed alone with HIP events (mean of reps; the
@@ -604,6 +636,7 @@ def main():
     if args.sweep:
         print("bench: large-head sweep", file=sys.stderr, flush=True)
         res["large_head_sweep"] = run_sweep(hs, synth, torch)
+        res["attention_split_gain"] = run_split_gain(hs, torch)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

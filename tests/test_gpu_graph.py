@@ -3,7 +3,9 @@
 Every entry point launches kernels on the caller's stream only: no allocation, no memset, no
 host synchronisation, and the active count comes from the host-side schedule.  So one whole
 iteration (selection, active set, gather, cache scatter or fused projection, attention,
-cached Euler update) can be captured once and replayed.  Each replay starts from the same
+cached Euler update) can be captured once and replayed, also with the fused active-set
+gather, the split attention and its merge kernel, and the allocation-free active set (whose
+scratch address is looked up by the eager call before the capture).  Each replay starts from the same
 state, with eager work and synchronisations between replays, and must reproduce the eager
 iteration bit for bit.
 """
@@ -46,20 +48,35 @@ def _state(hs):
         "group_id": torch.empty(N, dtype=torch.int32, device="cuda"),
         "active_idx": torch.empty(N, dtype=torch.int32, device="cuda"),
         "active_pos": torch.empty(N, dtype=torch.int32, device="cuda"),
-        "x_act": torch.empty((na, C), dtype=torch.float32, device="cuda"),
+        "x_act": torch.zeros((N, C), dtype=torch.float32, device="cuda"),
         "v_fresh": torch.empty((na, C), dtype=torch.float32, device="cuda"),
         "q_proj": torch.empty((1, na, H, D), dtype=torch.int16, device="cuda"),
         "out": torch.empty((1, na, H, D), dtype=torch.int16, device="cuda"),
         "ws": hs.workspace(N, len(SIZES)),
+        "attn_ws": hs.attention_workspace(na, N, 1, H, D),
     }
     return st, na
 
 
-def _iteration(hs, st, fused):
+def _iteration(hs, st, variant):
+    """variant: "plain" (separate calls), "fused" (projection with the cache write),
+    "ws" (active set fused with the latent gather; attention with a workspace, whose tiles are
+    all split here: 2 query tiles on a 256-CU chip), "noalloc" (the allocation-free active
+    set)."""
+    fused = variant == "fused"
     hs.hsa_select_groups(st["v_prev"], st["v_cur"], SIZES, st["group_id"], None, st["ws"])
-    na = hs.hsa_active_set(st["group_id"], BUDGETS, SIZES, T, M, ITER, st["active_idx"],
-                           st["active_pos"], st["ws"])
-    hs.hsastep_gather_rows(st["x_act"], st["x"], st["active_idx"], na)
+    if variant == "ws":
+        na = hs.hsa_active_set_gather(st["group_id"], BUDGETS, SIZES, T, M, ITER,
+                                      st["active_idx"], st["active_pos"], st["x"], st["x_act"],
+                                      st["ws"])
+    else:
+        if variant == "noalloc":
+            na = hs.hsa_active_set_noalloc(st["group_id"], BUDGETS, SIZES, T, M, ITER,
+                                           st["active_idx"], st["active_pos"])
+        else:
+            na = hs.hsa_active_set(st["group_id"], BUDGETS, SIZES, T, M, ITER, st["active_idx"],
+                                   st["active_pos"], st["ws"])
+        hs.hsastep_gather_rows(st["x_act"], st["x"], st["active_idx"], na)
     hs.hsastep_gather_rows(st["v_fresh"], st["v_model"], st["active_idx"], na)
     if fused:
         hs.hsa_qkv_project(st["x_model"], st["w"], st["bias"], st["q_proj"], st["k_cache"],
@@ -69,7 +86,11 @@ def _iteration(hs, st, fused):
         hs.hsa_kv_update(st["k_cache"], st["v_cache"], st["k_new"], st["v_new"],
                          st["active_idx"], na)
         q = st["q"]
-    hs.hsa_attention_active(q, st["k_cache"], st["v_cache"], st["out"], 1.0 / np.sqrt(D))
+    if variant == "ws":
+        hs.hsa_attention_active_ws(q, st["k_cache"], st["v_cache"], st["out"], 1.0 / np.sqrt(D),
+                                   st["attn_ws"])
+    else:
+        hs.hsa_attention_active(q, st["k_cache"], st["v_cache"], st["out"], 1.0 / np.sqrt(D))
     hs.hsa_euler_step(st["x"], st["v_hat"], st["v_fresh"], st["active_pos"], na, 0.625, 0.5)
 
 
@@ -77,7 +98,7 @@ OUTPUTS = ("group_id", "active_idx", "active_pos", "x_act", "v_fresh", "q_proj",
            "v_cache", "out", "x", "v_hat")
 
 
-@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("fused", ["plain", "fused", "ws", "noalloc"])
 def test_iteration_graph_replays_match_eager(hs, fused):
     st, na = _state(hs)
     assert 0 < na < N
@@ -121,7 +142,7 @@ def test_iteration_on_a_side_stream_matches(hs):
     st["q_proj"].zero_()
     st["out"].zero_()
     initial = {k: t.clone() for k, t in st.items()}
-    _iteration(hs, st, fused=False)
+    _iteration(hs, st, "plain")
     torch.cuda.synchronize()
     want = {k: st[k].clone() for k in OUTPUTS}
     for k, t in initial.items():
@@ -129,7 +150,7 @@ def test_iteration_on_a_side_stream_matches(hs):
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
-        _iteration(hs, st, fused=False)
+        _iteration(hs, st, "plain")
     side.synchronize()
     for k in OUTPUTS:
         assert torch.equal(st[k], want[k]), f"{k} differs on the side stream"
