@@ -2,7 +2,7 @@
 """Benchmark of one HSA denoise iteration on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-loop]
-                    [--no-streaming] [--pair] [--sweep] [--proj]
+                    [--no-streaming] [--pair] [--sweep] [--split] [--proj]
 
 A step is one pass of the whole path over the single-step workload (N = 32760
 tokens on a 21x30x52 latent grid, 12 heads x 128, 64 latent channels, half of
@@ -63,6 +63,10 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="also time the large-head sweep: N=75600, 40x128 heads, active fraction "
                         "1, 1/2, 1/4, 1/8 (attention, selection, scatter, Euler per kernel)")
+    p.add_argument("--split", action="store_true",
+                   help="also time attention with and without the split-key workspace on the "
+                        "shapes whose last round of query tiles leaves compute units idle, and "
+                        "the pair's dense launch over the same cache (included in --sweep)")
     p.add_argument("--proj", action="store_true",
                    help="also time the fused QKV projection with the cache write "
                         "(hsa_qkv_project) against library linear + hsa_kv_update")
@@ -451,7 +455,9 @@ def run_proj(hs, torch, reps=10):
 def run_split_gain(hs, torch, reps=5):
     """Attention with and without the workspace in the same run, for the shapes whose last
     round of query tiles leaves compute units idle: the full schedule at 25% and 75% active,
-    the aggressive pair at 10%, the sweep at f = 1 and 1/4 (seeded N(0,1) data, one layer)."""
+    the aggressive pair at 10%, the sweep at f = 1 and 1/4 (seeded N(0,1) data, one layer).
+    For the pair, the dense launch (every token active) over the same cache is timed too, so
+    that the 10%-active rate can be set against the dense rate of the same K/V stream."""
     dev = torch.device("cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = {"compute_units": cus, "points": []}
@@ -470,13 +476,27 @@ def run_split_gain(hs, torch, reps=5):
         flops = 4.0 * B * A * N * H * 128
         t_plain = _event_ms(torch, lambda: hs.hsa_attention_active(q, kc, vc, o, scale), reps)
         t_ws = _event_ms(torch, lambda: hs.hsa_attention_active_ws(q, kc, vc, o, scale, ws), reps)
-        out["points"].append({
-            "shape": name, "batch": B, "n_active": A, "n_tokens": N, "heads": H,
-            "plan": list(hs.hsastep_attention_plan(A, N, B, H, 128, cus, ws.numel())),
-            "ms_without_workspace": t_plain, "ms_with_workspace": t_ws,
-            "tflops_without": flops / t_plain / 1e9, "tflops_with": flops / t_ws / 1e9})
+        pt = {"shape": name, "batch": B, "n_active": A, "n_tokens": N, "heads": H,
+              "plan": list(hs.hsastep_attention_plan(A, N, B, H, 128, cus, ws.numel())),
+              "ms_without_workspace": t_plain, "ms_with_workspace": t_ws,
+              "tflops_without": flops / t_plain / 1e9, "tflops_with": flops / t_ws / 1e9}
         print(f"bench: split {name}: {t_plain:.3f} -> {t_ws:.3f} ms", file=sys.stderr, flush=True)
-        del q, kc, vc, o, ws
+        del q, o, ws
+        if name.startswith("aggressive pair"):
+            qd = torch.randn((B, N, H, 128), device=dev, generator=gen).to(torch.bfloat16)
+            od = torch.empty_like(qd)
+            wsd = hs.attention_workspace(N, N, B, H, 128, dev)
+            t_dense = _event_ms(torch, lambda: hs.hsa_attention_active_ws(qd, kc, vc, od, scale, wsd), 2)
+            fd = 4.0 * B * N * N * H * 128
+            pt["dense_ms_same_cache"] = t_dense
+            pt["dense_tflops_same_cache"] = fd / t_dense / 1e9
+            pt["with_workspace_frac_of_dense"] = pt["tflops_with"] / pt["dense_tflops_same_cache"]
+            pt["without_workspace_frac_of_dense"] = pt["tflops_without"] / pt["dense_tflops_same_cache"]
+            print(f"bench: split {name}: dense over the same cache {t_dense:.3f} ms", file=sys.stderr,
+                  flush=True)
+            del qd, od, wsd
+        out["points"].append(pt)
+        del kc, vc
     return out
 
 
@@ -636,6 +656,8 @@ def main():
     if args.sweep:
         print("bench: large-head sweep", file=sys.stderr, flush=True)
         res["large_head_sweep"] = run_sweep(hs, synth, torch)
+    if args.sweep or args.split:
+        print("bench: split-key attention", file=sys.stderr, flush=True)
         res["attention_split_gain"] = run_split_gain(hs, torch)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
