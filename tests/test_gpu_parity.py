@@ -302,8 +302,10 @@ def test_tiny_loop_reselect(hs):
 
 
 def test_single_step_full_size(hs):
-    """N = 32760, 12 x 128 heads, half the tokens active: the measured configuration, with
-    every output compared in full except attention (64 sampled query rows)."""
+    """N = 32760, 12 x 128 heads, half the tokens active: the measured configuration, through
+    the same calls the benchmark step makes (the active set fused with the latent-row gather,
+    attention through the workspace entry point), with every output compared in full except
+    attention (64 sampled query rows)."""
     cfg = synth.single_step()
     N, C, H, D, i = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim, cfg.iteration
     model = SyntheticModel(cfg, hs)
@@ -314,11 +316,17 @@ def test_single_step_full_size(hs):
     hs.hsa_select_groups(dev(vp), dev(vc), cfg.sizes, g, None, ws)
     idx = torch.empty(N, dtype=torch.int32, device="cuda")
     pos = torch.empty(N, dtype=torch.int32, device="cuda")
-    na = hs.hsa_active_set(g, cfg.budgets, cfg.sizes, cfg.T, cfg.m, i, idx, pos, ws)
+    x0 = synth.latent0(cfg)
+    xd = dev(x0)
+    x_act = torch.full((N, C), np.nan, dtype=torch.float32, device="cuda")
+    na = hs.hsa_active_set_gather(g, cfg.budgets, cfg.sizes, cfg.T, cfg.m, i, idx, pos, xd,
+                                  x_act, ws)
     idx_w, pos_w = oracle.active_set(g_want, cfg.budgets, cfg.T, cfg.m, i)
     assert na == 16380 == idx_w.shape[0]
     assert np.array_equal(host(g), g_want)
     assert np.array_equal(host(idx)[:na], idx_w) and np.array_equal(host(pos), pos_w)
+    assert np.array_equal(host(x_act)[:na].view(np.uint32), x0[idx_w].view(np.uint32))
+    assert np.isnan(host(x_act)[na:]).all()       # rows past |A| untouched
 
     pre = model.src.prefill(0)
     q, kn, vn = (model.src.rows(t, 0, i, na) for t in ("q", "k", "v"))
@@ -330,14 +338,14 @@ def test_single_step_full_size(hs):
 
     o = torch.empty((1, na, H, D), dtype=torch.int16, device="cuda")
     scale = float(np.float32(1.0 / np.sqrt(D)))
-    hs.hsa_attention_active(bits_dev(q), kd, vd, o, scale)
+    hs.hsa_attention_active_ws(bits_dev(q), kd, vd, o, scale,
+                               hs.attention_workspace(na, N, 1, H, D))
     rows = synth.sample_rows(cfg.cfg_id, na, 64)
     want = oracle.attention_active(q[:, rows], kc, vc_, scale)
     attn_close(host_bits(o)[:, rows], want, "single step sampled rows")
 
-    x0 = synth.latent0(cfg)
     vhat0 = vp
-    xd, vhd = dev(x0), dev(vhat0)
+    vhd = dev(vhat0)
     vfresh = model.velocity(i, idx, na)
     sig = oracle.sigma_schedule(cfg.T)
     hs.hsa_euler_step(xd, vhd, vfresh, pos, na, float(sig[i]), float(sig[i + 1]))
@@ -353,11 +361,29 @@ def test_aggressive_pair_full_size_loop(hs):
     in full at every iteration.  At iteration 37 (10% of the tokens active, so most cache rows
     are stale) sampled cache rows are compared with the replay rule (a row holds the K/V of the
     last iteration that had its token active, else the prefill) and attention with the oracle
-    on sampled query rows, the oracle's caches rebuilt by that rule."""
-    from sparse_attention_l1_amd.sampler import HsaSampler
+    on sampled query rows, the oracle's caches rebuilt by that rule.  The sampler's attention
+    splits the key range of the last round's query tiles at that iteration (2304 whole tiles,
+    96 split in 5)."""
     cfg = synth.aggressive_pair()
+    assert hs.hsastep_attention_plan(cfg.sizes[0], cfg.n_tokens, cfg.batch, cfg.heads,
+                                     cfg.head_dim, 256, 1 << 40)[2] > 1
+    _full_size_loop(hs, cfg, 37, "pair loop")
+
+
+def test_full_schedule_full_size_loop(hs):
+    """N = 32760, 12 x 128 heads, T = 40, four groups of 25% with budgets {40, 20, 10, 5},
+    m = 4, one layer of the 30-layer stack: the whole 40-iteration loop through the C ABI, with
+    the checks of the pair loop at iteration 33, where only G_1 is active (25%: 384 query
+    tiles, so the last round's 128 tiles split their key range in two)."""
+    cfg = synth.full_schedule()
+    assert hs.hsastep_attention_plan(cfg.sizes[0], cfg.n_tokens, cfg.batch, cfg.heads,
+                                     cfg.head_dim, 256, 1 << 40)[2] > 1
+    _full_size_loop(hs, cfg, 33, "full schedule loop")
+
+
+def _full_size_loop(hs, cfg, check_i, tag):
+    from sparse_attention_l1_amd.sampler import HsaSampler
     N, H, D, T, B = cfg.n_tokens, cfg.heads, cfg.head_dim, cfg.T, cfg.batch
-    check_i = 37
     model = SyntheticModel(cfg, hs)
     scale = float(np.float32(1.0 / np.sqrt(D)))
     rec = {}
@@ -387,7 +413,7 @@ def test_aggressive_pair_full_size_loop(hs):
         torch.cuda.synchronize()
         want = rec[i]
         na = smp.n_active
-        print(f"[pair loop] iteration {i}: {na} active", flush=True)
+        print(f"[{tag}] iteration {i}: {na} active", flush=True)
         assert na == want["active_idx"].shape[0], f"iteration {i}"
         assert np.array_equal(host(smp.active_idx)[:na], want["active_idx"]), f"iteration {i}"
         assert np.array_equal(host(smp.group_id), want["group_id"]), f"iteration {i}"
@@ -415,7 +441,7 @@ def test_aggressive_pair_full_size_loop(hs):
     na = rec[check_i]["active_idx"].shape[0]
     q = model.src.rows("q", 0, check_i, na)[:, qrows]
     want = oracle.attention_active(q, caches["k"], caches["v"], scale)
-    attn_close(got["attn"], want, f"pair loop i{check_i} sampled rows")
+    attn_close(got["attn"], want, f"{tag} i{check_i} sampled rows")
 
 
 # ----------------------------------------------------------------------------- active set + gather
