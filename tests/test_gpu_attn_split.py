@@ -73,6 +73,35 @@ def test_split_attention_matches_oracle(hs, B, A, N, H, qs, rows):
     assert diff <= 2e-2
 
 
+def test_split_attention_sweep_shape(hs):
+    """The large-head sweep's shape at f = 1/4 (B = 1, |A| = 18900 of N = 75600 tokens,
+    40 x 128 heads): 2960 tiles, the last round's 144 split in 3 key ranges.  Inputs are seeded
+    N(0,1) values drawn on the device (as the benchmark's sweep draws them); 16 sampled query
+    rows are compared with the oracle, and every row with the unsplit kernel."""
+    B, A, N, H = 1, 18900, 75600, 40
+    g = torch.Generator(device="cuda").manual_seed(20260512)
+    draw = lambda *shape: torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    qd, kd, vd = draw(B, A, H, 128), draw(B, N, H, 128), draw(B, N, H, 128)
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    ws = hs.attention_workspace(A, N, B, H, 128)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = hs.hsastep_attention_plan(A, N, B, H, 128, cus, ws.numel())
+    print(f"[split] sweep shape: plan {plan} on {cus} CUs", flush=True)
+    o = torch.full((B, A, H, 128), 0x7F7F, dtype=torch.int16, device="cuda")
+    o_plain = torch.empty_like(o)
+    hs.hsa_attention_active_ws(qd, kd, vd, o, scale, ws)
+    hs.hsa_attention_active(qd, kd, vd, o_plain, scale)
+    torch.cuda.synchronize()
+    sel = synth.sample_rows(98, A, 16)
+    bits = lambda t: t.cpu().numpy().view(np.uint16)
+    want = oracle.attention_active(bits(qd)[:, sel], bits(kd), bits(vd), scale)
+    got = host_bits(o)
+    attn_close(got[:, sel], want, "split sweep shape f=1/4")
+    diff = float(np.max(np.abs(synth_bf16_to_f64(got) - synth_bf16_to_f64(host_bits(o_plain)))))
+    print(f"[split] sweep shape: max |split - unsplit| {diff:.3e}", flush=True)
+    assert diff <= 2e-2
+
+
 def synth_bf16_to_f64(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
