@@ -38,7 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_single_step_pmc.txt")
 # sources of the attention kernels: the counters summary is valid only for this exact code
-# (the two HIP files and the key loop the generator emits; not the generator's comments)
+# (the two HIP files and the two key loops the generator emits; not the generator's comments)
 ATTN_SRCS = [os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", f)
              for f in ("attn.hip", "attn_pipe.hip")]
 
@@ -97,7 +97,7 @@ def attn_source_hash() -> str:
         "attn_loop_gen", os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", "attn_loop_gen.py"))
     gen = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(gen)
-    h.update("\n".join(gen.generate()).encode())
+    h.update("\n".join(gen.generate(True) + gen.generate(False)).encode())
     h.update(gen.clobber_list().encode())
     return h.hexdigest()[:16]
 

@@ -45,6 +45,7 @@ Register map (per lane):  VGPR  S 0-63, P 64-95, K fragments 96-159, LDS/buffer 
 160-183, softmax state 184-194, temps 196-218;  AGPR  O 0-127, Q^T 128-191, V^T fragments
 192-255;  SGPR 40-77 (descriptors, counters, routine addresses).
 """
+import re
 import sys
 
 # ---------------------------------------------------------------- register map
@@ -258,6 +259,30 @@ def check_pair_and_fix(blocks, label):
             f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(LS + qb)}"]
 
 
+def add_block_sums(*blocks):
+    """L += LS for each (parity, query block) without a range check (the fast body)."""
+    return [f"v_add_f32 {v(L + qb)}, {v(L + qb)}, {v(LS + qb)}" for _, qb in blocks]
+
+
+def init_reference_max(par, qb):
+    """Sets the reference max of query block qb to the true max of its S^T block (both lanes of a
+    query), before any of that query's exponentials: the fast body never raises it in the
+    loop, so every later p is 2^(c s - m) against this block's max."""
+    sb = S(par, qb)
+    t1, t3 = T0 + 1, T0 + 3
+    out = [f"v_max3_f32 {v(t1)}, {v(sb)}, {s(NINF)}, {v(sb + 1)}"]
+    for j in range(2, 16, 2):
+        out.append(f"v_max3_f32 {v(t1)}, {v(t1)}, {v(sb + j)}, {v(sb + j + 1)}")
+    out += ["s_waitcnt lgkmcnt(0)",
+            f"ds_bpermute_b32 {v(t3)}, {v(VAX)}, {v(t1)}",
+            "s_waitcnt lgkmcnt(0)",
+            f"v_max_f32 {v(t3)}, {v(t1)}, {v(t3)}",
+            f"v_mul_f32 {v(t3)}, {s(SC)}, {v(t3)}",
+            f"v_mov_b32 {v(M + qb)}, {v(t3)}",
+            f"v_xor_b32 {v(NEGM + qb)}, 0x80000000, {v(t3)}"]
+    return out
+
+
 def mask_call(par, qb, stepreg, label):
     return ([f"s_cmp_eq_u32 {s(STEP)}, {s(stepreg)}"] +
             call_site("s_cbranch_scc1", s(MASKA + 2 * (par * 2 + qb), 2), label))
@@ -302,8 +327,9 @@ def place(ops, slots):
 
 
 # ---------------------------------------------------------------- one pipelined step
-def step(r):
-    """Step s with s % 8 == r: every buffer index and LDS offset is static for a given r."""
+def step(r, checked=True):
+    """Step s with s % 8 == r: every buffer index and LDS offset is static for a given r.
+    Unchecked (the fast body), the two block sums go into L without the range check."""
     p, q = r & 1, (r & 1) ^ 1
     x1 = r + 1            # V block read in H1 (block s + 1: same parity and tile position)
     x3 = r + 3            # K block read in H2 (block s + 3)
@@ -338,7 +364,10 @@ def step(r):
             out.append(loads[li][1])
             li += 1
     # the range checks of the two blocks whose softmax ends here, with one branch
-    out.extend(check_pair_and_fix(((q, 0), (p, 1)), f".Lf{r}"))
+    if checked:
+        out.extend(check_pair_and_fix(((q, 0), (p, 1)), f".Lf{r}"))
+    else:
+        out.extend(add_block_sums((q, 0), (p, 1)))
     # ---------------- H2: PV(s,1) [VF[p], P[p][1]] and PV(s+1,0) [VF[q], P[q][0]]
     kr = [kread(x3, u) for u in range(8)]
     valu = (mask_call(q, 1, MASK1, f".Lm{r}a") + mask_call(p, 0, MASK0, f".Lm{r}b") +
@@ -432,11 +461,12 @@ def mask_routine(par, qb):
 
 
 # ---------------------------------------------------------------- prologue / epilogue
-def prologue():
+def prologue(checked=True):
     """Loads V tiles 0, 1 and K tiles -1 (blocks 0, 1 only) and 0; computes S(0, *) and
     S(1, 0), the whole softmax of (0, 0), PV(0, 0), pairs 0..3 of softmax(0, 1) and (1, 0);
     reads K(2) and V(0); then refills K buffer 1 with K tile 1.  Leaves the state step 0
-    expects."""
+    expects.  Unchecked, the reference max of both query blocks is first set from key
+    block 0."""
     out = ["; ---- prologue",
            f"s_mov_b32 {s(M0SAVE)}, m0",
            f"s_mov_b32 {s(NINF)}, 0xff800000",
@@ -479,8 +509,11 @@ def prologue():
             out.append("s_waitcnt lgkmcnt(7)")
         out.extend(vr[2 * u:2 * u + 2])
     out += ["s_nop 7"]
+    if not checked:
+        out += ["s_nop 7", "s_nop 7"]           # the S(0, 1) MFMAs just issued -> VALU reads
+        out += init_reference_max(0, 0) + init_reference_max(0, 1)
     out.extend(softmax_full(0, 0))
-    out.extend(check_and_fix(0, 0, ".Lfp0"))
+    out.extend(check_and_fix(0, 0, ".Lfp0") if checked else add_block_sums((0, 0)))
     out.append("s_waitcnt lgkmcnt(0)")
     out.append("s_nop 1")
     for h2 in range(2):
@@ -496,14 +529,14 @@ def prologue():
     return out
 
 
-def epilogue():
+def epilogue(checked=True):
     """After the last step (s = n_blocks - 2): pairs 4..7 of softmax(s+1, 1), then PV(s+1, 1)."""
     out = []
     for x in range(2):
         out.append(f".Lexit{x}:")
         out.append("s_waitcnt lgkmcnt(0)")
         out.extend(softmax_part(x, 1, 4, 8))
-        out.extend(check_and_fix(x, 1, f".Lfe{x}"))
+        out.extend(check_and_fix(x, 1, f".Lfe{x}") if checked else add_block_sums((x, 1)))
         out.append("s_nop 1")
         for h2 in range(2):
             for e in range(4):
@@ -512,15 +545,17 @@ def epilogue():
     return out
 
 
-def generate():
-    """The whole asm body, one instruction or label per list entry."""
+def generate(checked=True):
+    """The whole asm body, one instruction or label per list entry.  checked=False gives the
+    fast body: no range check inside the loop, every label renamed (.LF...) so that both
+    bodies can sit in one kernel."""
     body = []
-    body.extend(prologue())
+    body.extend(prologue(checked))
     body.append(".Lloop:")
     for r in range(8):
-        body.extend(step(r))
+        body.extend(step(r, checked))
     body.append("s_branch .Lloop")
-    body.extend(epilogue())
+    body.extend(epilogue(checked))
     for par in range(2):
         for qb in range(2):
             body.extend(fix_routine(par, qb))
@@ -531,6 +566,8 @@ def generate():
              f"s_mov_b32 m0, {s(M0SAVE)}",
              "s_nop 15",                        # MFMA results -> the compiler's reads of O
              "s_nop 7"]
+    if not checked:
+        body = [re.sub(r"\.L(\w+)", r".LF\1", l) for l in body]
     return body
 
 
@@ -550,14 +587,14 @@ def clobber_list():
 
 
 def write(path):
-    body = generate()
     with open(path, "w") as f:
-        f.write("// Generated by attn_loop_gen.py: the key loop of attn_pipe.hip (inline asm body).\n")
-        f.write("#define HSA_ATTN_LOOP_ASM \\\n")
-        for l in body:
-            l2 = l.replace("\\", "\\\\").replace('"', '\\"')
-            f.write(f'  "{l2}\\n" \\\n')
-        f.write("  \"\"\n")
+        f.write("// Generated by attn_loop_gen.py: the key loop of attn_pipe.hip (inline asm bodies).\n")
+        for name, checked in (("HSA_ATTN_LOOP_ASM", True), ("HSA_ATTN_LOOP_FAST_ASM", False)):
+            f.write(f"#define {name} \\\n")
+            for l in generate(checked):
+                l2 = l.replace("\\", "\\\\").replace('"', '\\"')
+                f.write(f'  "{l2}\\n" \\\n')
+            f.write("  \"\"\n")
         f.write(f"#define HSA_ATTN_LOOP_CLOBBERS {clobber_list()}\n")
 
 

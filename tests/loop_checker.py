@@ -202,13 +202,14 @@ def expand(gen, lines, body, take_calls):
     return out
 
 
-def traces(gen):
+def traces(gen, checked=True):
     """(name, instruction list) for the paths through the loop: the prologue, n steps, the exit
-    after the last one, with every call skipped or taken."""
-    body = gen.generate()
-    pro = gen.prologue()
-    steps = [gen.step(r) for r in range(8)]
-    epi = gen.epilogue()
+    after the last one, with every call skipped or taken.  checked=False walks the fast body
+    (its labels carry an F after .L, taken off here to match the step lists)."""
+    body = [l.replace(".LF", ".L") for l in gen.generate(checked)]
+    pro = gen.prologue(checked)
+    steps = [gen.step(r, checked) for r in range(8)]
+    epi = gen.epilogue(checked)
     exits = []
     for x in range(2):
         i = epi.index(f".Lexit{x}:")
@@ -223,9 +224,9 @@ def traces(gen):
             yield f"calls={take} last_step={last}", expand(gen, t, body, take)
 
 
-def check_hazards(gen):
+def check_hazards(gen, checked=True):
     errors = []
-    for name, t in traces(gen):
+    for name, t in traces(gen, checked):
         c = Checker(name)
         c.run(t)
         errors += c.errors
@@ -244,10 +245,10 @@ def declared_registers(hip_source, gen):
     return decl
 
 
-def check_registers(gen, hip_source):
+def check_registers(gen, hip_source, checked=True):
     decl = declared_registers(hip_source, gen)
     bad = set()
-    for line in gen.generate():
+    for line in (gen.generate() if checked else gen.generate(False)):
         p = parse(line)
         if p is None:
             continue
@@ -258,13 +259,13 @@ def check_registers(gen, hip_source):
     return sorted(bad)
 
 
-def check_lds_bounds(gen):
+def check_lds_bounds(gen, checked=True):
     """Largest byte an LDS read or a tile load can touch, over all lanes."""
     errors = []
     kmax = max(lq * 256 + 16 * (c ^ ((4 * (lq & 3)) + ((lq >> 2) & 3)))
                for lq in range(32) for c in range(16)) + 16
     vmax = 65536 + 15 * 256 + 16 * 15 + 8 + 8
-    for line in gen.generate():
+    for line in (gen.generate() if checked else gen.generate(False)):
         m = re.search(r"offset:(\d+)", line)
         if line.startswith("ds_read_b128") and m and kmax + int(m.group(1)) > LDS_BYTES:
             errors.append(line)

@@ -15,16 +15,38 @@ GEN = lc.load_generator()
 HIP = open(os.path.join(lc.CSRC, "attn_pipe.hip")).read()
 
 
-def test_hazards_and_lds_counters():
-    assert lc.check_hazards(GEN) == []
+@pytest.mark.parametrize("checked", [True, False], ids=["checked", "fast"])
+def test_hazards_and_lds_counters(checked):
+    assert lc.check_hazards(GEN, checked) == []
 
 
-def test_registers_are_declared():
-    assert lc.check_registers(GEN, HIP) == []
+@pytest.mark.parametrize("checked", [True, False], ids=["checked", "fast"])
+def test_registers_are_declared(checked):
+    assert lc.check_registers(GEN, HIP, checked) == []
 
 
-def test_lds_offsets_in_bounds():
-    assert lc.check_lds_bounds(GEN) == []
+@pytest.mark.parametrize("checked", [True, False], ids=["checked", "fast"])
+def test_lds_offsets_in_bounds(checked):
+    assert lc.check_lds_bounds(GEN, checked) == []
+
+
+def test_fast_body_shape():
+    """The fast body: the same loop without any range check or data-dependent branch, its
+    labels distinct from the checked body's, and each query block's reference max set from
+    key block 0 before that block's first exponential."""
+    fast, checked = GEN.generate(False), GEN.generate(True)
+    assert not any(l.startswith(("s_cbranch_vccnz", "v_cmp_nge_f32")) for l in fast)
+    assert any(l.startswith("s_cbranch_vccnz") for l in checked)
+    labels = lambda body: {l[:-1] for l in body if l.endswith(":")}
+    assert labels(fast) and not labels(fast) & labels(checked)
+    loop_f = fast[fast.index(".LFloop:"):fast.index("s_branch .LFloop")]
+    loop_c = checked[checked.index(".Lloop:"):checked.index("s_branch .Lloop")]
+    strip = lambda body: [l for l in body if l.startswith(("v_mfma", "ds_read", "buffer_load", "s_barrier", "v_exp"))]
+    assert strip(loop_f) == strip(loop_c)
+    first_exp = next(i for i, l in enumerate(fast) if l.startswith("v_exp_f32"))
+    for qb in (0, 1):
+        sets_m = [i for i, l in enumerate(fast) if l.startswith(f"v_mov_b32 v{GEN.M + qb},")]
+        assert sets_m and sets_m[0] < first_exp
 
 
 def test_loop_shape():
@@ -53,7 +75,7 @@ def _with_patch(name, fn):
 
 
 def test_checker_catches_a_missing_lds_wait():
-    errs = _with_patch("step", lambda f: lambda r: [l for l in f(r) if "lgkmcnt(8)" not in l])
+    errs = _with_patch("step", lambda f: lambda *a: [l for l in f(*a) if "lgkmcnt(8)" not in l])
     assert any("LDS result is in flight" in e for e in errs)
 
 
@@ -75,8 +97,8 @@ def test_checker_catches_a_missing_wait_state():
 def test_checker_catches_an_early_mfma_read():
     # VALU reading an S^T accumulator right after the MFMA chain that writes it
     def early(f):
-        def g(r):
-            out = f(r)
+        def g(*a):
+            out = f(*a)
             hits = [k for k, l in enumerate(out) if l.startswith("v_mfma") and "v[0:15]" in l.split(",")[0]]
             if not hits:
                 return out

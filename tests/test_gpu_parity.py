@@ -199,6 +199,41 @@ def test_attention_late_outlier_key(hs, N, D, late):
     assert not np.isnan(bf16_to_f64(host_bits(o))).any()
 
 
+@pytest.mark.parametrize("N", [1000, 5000])
+def test_attention_fallback_per_query(hs, N):
+    """Every third query meets keys about 400 (base 2) above its first key block's max, so
+    p against that block's reference would overflow fp32: those queries leave the fast body
+    out of range and are redone by the checked body, while their tile neighbours keep the fast
+    result.  Against the oracle, the bits of a query do not depend on its neighbours (a launch
+    of every second query gives the same rows), and the same holds through the split path."""
+    B, A, H, D = 1, 300, 2, 128
+    r = np.random.default_rng(N + 5)
+    qf = r.standard_normal((B, A, H, D)).astype(np.float32)
+    kf = r.standard_normal((B, N, H, D)).astype(np.float32)
+    qf[:, ::3, :, 0] = 40.0
+    kf[:, :, :, 0] = 0.0
+    for j in (N // 2, N - 37):
+        kf[:, j, :, 0] = 80.0
+    q, k = synth.f32_to_bf16_bits(qf), synth.f32_to_bf16_bits(kf)
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, N, H, D)).astype(np.float32))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    want = oracle.attention_active(q, k, v, scale)
+    o = torch.empty((B, A, H, D), dtype=torch.int16, device="cuda")
+    hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
+    torch.cuda.synchronize()
+    attn_close(host_bits(o), want, f"fallback per query N{N}")
+    sub = np.arange(0, A, 2)
+    o2 = torch.empty((B, sub.size, H, D), dtype=torch.int16, device="cuda")
+    hs.hsa_attention_active(bits_dev(q[:, sub]), bits_dev(k), bits_dev(v), o2, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(o2), host_bits(o)[:, sub])
+    ws = hs.attention_workspace(A, N, B, H, D)
+    o3 = torch.empty_like(o)
+    hs.hsa_attention_active_ws(bits_dev(q), bits_dev(k), bits_dev(v), o3, scale, ws)
+    torch.cuda.synchronize()
+    attn_close(host_bits(o3), want, f"fallback per query, split, N{N}")
+
+
 def test_attention_zero_query_is_mean(hs):
     B, A, N, H, D = 1, 5, 999, 2, 128
     r = np.random.default_rng(1)
