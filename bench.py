@@ -38,7 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_PMC_SUMMARY = os.path.join(ROOT, "profiles", "attention_single_step_pmc.txt")
 # sources of the attention kernels: the counters summary is valid only for this exact code
-# (the two HIP files and the two key loops the generator emits; not the generator's comments)
+# (the code of the two HIP files and the two key loops the generator emits; not comments)
 ATTN_SRCS = [os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", f)
              for f in ("attn.hip", "attn_pipe.hip")]
 
@@ -92,7 +92,9 @@ def attn_source_hash() -> str:
     import importlib.util
     h = hashlib.sha256()
     for f in ATTN_SRCS:
-        h.update(open(f, "rb").read())
+        # code only: a comment edit does not invalidate the counters
+        code = [ln.split("//", 1)[0].rstrip() for ln in open(f, encoding="utf-8").read().splitlines()]
+        h.update("\n".join(ln for ln in code if ln).encode())
     spec = importlib.util.spec_from_file_location(
         "attn_loop_gen", os.path.join(ROOT, "sparse_attention_l1_amd", "csrc", "attn_loop_gen.py"))
     gen = importlib.util.module_from_spec(spec)

@@ -41,6 +41,12 @@ the running sum is per lane; the two lanes of a query add theirs at the end.  (R
 16x16x32 or 4x4x4 MFMAs on the packed P, with a 0/1 operand, cost 11-19% of the kernel's time:
 more than these 24 extra VALU instructions per block.)
 
+Two bodies: generate(True) is the checked loop described above; generate(False) is the fast
+loop, which sets each query block's reference max from key block 0 in the prologue and then
+drops every range check (the block sums only go into L), so no step has a data-dependent
+branch.  Its labels carry an F after .L so that both bodies can sit in one kernel; the kernel
+runs the checked body only for workgroups with a query whose fast row sum left [1, 2^64].
+
 Register map (per lane):  VGPR  S 0-63, P 64-95, K fragments 96-159, LDS/buffer addresses
 160-183, softmax state 184-194, temps 196-218;  AGPR  O 0-127, Q^T 128-191, V^T fragments
 192-255;  SGPR 40-77 (descriptors, counters, routine addresses).
