@@ -197,6 +197,8 @@ int hsa_kv_update(uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_new,
  *   out                [batch, n_active, heads, head_dim] bf16 output
  * head_dim in {64, 128}; n_tokens >= 1; softmax_scale finite and > 0
  * (1/sqrt(head_dim) in the usual model).  n_active == 0 is a no-op.
+ * Deterministic: repeated calls give the same bits, and a query's output does not depend on
+ * the other queries of the launch (a launch of any subset of the rows gives the same rows).
  */
 int hsa_attention_active(const uint16_t* q_active, const uint16_t* k_cache,
                          const uint16_t* v_cache, uint16_t* out, int64_t n_active,
