@@ -234,6 +234,28 @@ def test_attention_fallback_per_query(hs, N):
     attn_close(host_bits(o3), want, f"fallback per query, split, N{N}")
 
 
+@pytest.mark.parametrize("D,N,key", [(128, 1000, 3), (128, 1000, 700), (64, 500, 300)])
+def test_attention_nan_key(hs, D, N, key):
+    """A NaN in one cached key of head 1 makes every score of that head NaN, so the oracle's
+    softmax is NaN for all of head 1's queries; the kernels give NaN there too (a NaN row sum
+    also sends the fast loop's queries to the checked loop), and head 0 is unaffected."""
+    B, A, H = 1, 300, 2
+    r = np.random.default_rng(N + key)
+    q = synth.f32_to_bf16_bits(r.standard_normal((B, A, H, D)).astype(np.float32))
+    k = synth.f32_to_bf16_bits(r.standard_normal((B, N, H, D)).astype(np.float32))
+    k[0, key, 1, 5] = 0x7FC0                      # a quiet NaN in bf16
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, N, H, D)).astype(np.float32))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    want = oracle.attention_active(q, k, v, scale)
+    assert np.isnan(want[:, :, 1]).all() and np.isfinite(want[:, :, 0]).all()
+    o = torch.empty((B, A, H, D), dtype=torch.int16, device="cuda")
+    hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
+    torch.cuda.synchronize()
+    got = bf16_to_f64(host_bits(o))
+    assert np.isnan(got[:, :, 1]).all()
+    attn_close(host_bits(o)[:, :, :1], want[:, :, :1], f"NaN key D{D} N{N} key {key}, head 0")
+
+
 def test_attention_zero_query_is_mean(hs):
     B, A, N, H, D = 1, 5, 999, 2, 128
     r = np.random.default_rng(1)
