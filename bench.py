@@ -342,10 +342,40 @@ def cpu_baseline(budget_s: float):
                        f"extrapolated step {t_step:.1f} s")}
 
 
-def run_loop(hs, synth, torch, cfg):
-    """A whole sampling run (all T iterations, every layer) through the C ABI with the synthetic
+def _timed_calls(hs, torch, names):
+    """Wraps the named entry points of the binding module so that every call is bracketed by a
+    HIP event pair on the current stream; returns (restore, records) with records[name] a list
+    of event pairs.  Used for one extra pass of a loop only: the events add a little work."""
+    records = {n: [] for n in names}
+    orig = {n: getattr(hs, n) for n in names}
+
+    def wrap(n):
+        f = orig[n]
+
+        def call(*a, **k):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r = f(*a, **k)
+            e1.record()
+            records[n].append((e0, e1))
+            return r
+        return call
+
+    for n in names:
+        setattr(hs, n, wrap(n))
+
+    def restore():
+        for n in names:
+            setattr(hs, n, orig[n])
+    return restore, records
+
+
+def run_loop(hs, synth, torch, cfg, reps=1, breakdown=False):
+    """Whole sampling runs (all T iterations, every layer) through the C ABI with the synthetic
     model stand-in (seeded Q/K/V pool windows and velocities, on the device): ms per iteration
-    (HIP events around each), and the attention FLOPs of the run over its wall time."""
+    (HIP events around each) over `reps` runs from the same initial state, and the attention
+    FLOPs of a run over its wall time.  With breakdown, one more run times every entry point
+    call (events around each) and reports ms per iteration per entry point."""
     from sparse_attention_l1_amd.sampler import HsaSampler
     dev = torch.device("cuda")
     N, C, H, D, B = cfg.n_tokens, cfg.channels, cfg.heads, cfg.head_dim, cfg.batch
@@ -355,6 +385,8 @@ def run_loop(hs, synth, torch, cfg):
     pre = torch.from_numpy(src.prefill(0).view(np.int16)).to(dev)
     del src.prefill_pool
     v_all = [torch.from_numpy(vm(i)).to(dev) for i in range(cfg.T)]
+    x0 = torch.from_numpy(synth.latent0(cfg)).to(dev)
+    vp = torch.from_numpy(vm.v_prev).to(dev)
 
     class PoolModel:
         def qkv(self, l, i, active_idx, na):
@@ -372,32 +404,59 @@ def run_loop(hs, synth, torch, cfg):
     vbuf = torch.empty((N, C), dtype=torch.float32, device=dev)
     smp = HsaSampler(n_tokens=N, channels=C, batch=B, heads=H, head_dim=D, layers=cfg.layers,
                      T=cfg.T, budgets=cfg.budgets, group_sizes=cfg.sizes, m=cfg.m)
-    smp.reset(torch.from_numpy(synth.latent0(cfg)).to(dev), torch.from_numpy(vm.v_prev).to(dev),
-              lambda l: (pre, pre))
     model = PoolModel()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(cfg.T)]
-    flops = 0.0
-    t0 = time.perf_counter()
-    for i in range(cfg.T):
-        evs[i][0].record()
-        smp.iteration(i, model)
-        evs[i][1].record()
-        flops += 4.0 * B * smp.n_active * N * H * D * cfg.layers
-        if B > 1 or cfg.layers > 30:
-            torch.cuda.synchronize()   # long iterations: report progress as they finish
-            print(f"bench: {cfg.name}: iteration {i} done, |A| = {smp.n_active}", file=sys.stderr,
-                  flush=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_iter = [a.elapsed_time(b) for a, b in evs]
-    return {"workload": cfg.name, "iterations": cfg.T, "layers": cfg.layers, "batch": B,
-            "ms_per_iteration_mean": float(np.mean(per_iter)),
-            "ms_per_iteration": [round(x, 3) for x in per_iter],
-            "ms_total": float(np.sum(per_iter)),
-            "attention_pflop": flops / 1e15, "tflops_effective": flops / wall / 1e12,
-            "wall_s": wall}
+
+    def one_run(tag):
+        smp.reset(x0, vp, lambda l: (pre, pre))
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(cfg.T)]
+        flops = 0.0
+        t0 = time.perf_counter()
+        for i in range(cfg.T):
+            evs[i][0].record()
+            smp.iteration(i, model)
+            evs[i][1].record()
+            flops += 4.0 * B * smp.n_active * N * H * D * cfg.layers
+            if B > 1 or cfg.layers > 30:
+                torch.cuda.synchronize()   # long iterations: report progress as they finish
+                print(f"bench: {cfg.name}{tag}: iteration {i} done, |A| = {smp.n_active}",
+                      file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return [a.elapsed_time(b) for a, b in evs], flops, wall
+
+    runs = []
+    for r in range(reps):
+        runs.append(one_run(f" run {r + 1}/{reps}"))
+        print(f"bench: {cfg.name}: run {r + 1}/{reps}: {np.mean(runs[-1][0]):.2f} ms per iteration",
+              file=sys.stderr, flush=True)
+    per_iter = np.mean([r[0] for r in runs], axis=0)
+    flops = runs[0][1]
+    wall = float(np.mean([r[2] for r in runs]))
+    out = {"workload": cfg.name, "iterations": cfg.T, "layers": cfg.layers, "batch": B,
+           "runs": reps,
+           "ms_per_iteration_mean": float(np.mean(per_iter)),
+           "ms_per_iteration_mean_per_run": [round(float(np.mean(r[0])), 3) for r in runs],
+           "ms_per_iteration": [round(float(x), 3) for x in per_iter],
+           "ms_total": float(np.sum(per_iter)),
+           "attention_pflop": flops / 1e15, "tflops_effective": flops / wall / 1e12,
+           "wall_s": wall}
+    if breakdown:
+        names = ["hsa_select_groups", "hsa_active_set_gather", "hsastep_gather_rows",
+                 "hsa_kv_update", "hsa_attention_active_ws", "hsa_euler_step"]
+        restore, rec = _timed_calls(hs, torch, names)
+        try:
+            t_iter, _, _ = one_run(" (per entry point)")
+        finally:
+            restore()
+        per = {n: sum(a.elapsed_time(b) for a, b in rec[n]) / cfg.T for n in names}
+        out["per_entry_point_ms_per_iteration"] = {
+            "note": "one extra run with HIP events around every call (the model's velocity rows "
+                    "come from hsastep_gather_rows, a stand-in for the model)",
+            "ms_per_iteration_of_that_run": float(np.mean(t_iter)),
+            **{n: round(v, 4) for n, v in per.items()}}
+    return out
 
 
 def run_proj(hs, torch, reps=10):
@@ -648,7 +707,8 @@ def main():
         res["streaming_kernels"] = run_streaming(hs, synth, torch, st)
     if not args.no_loop:
         print("bench: full schedule loop", file=sys.stderr, flush=True)
-        res["full_schedule"] = run_loop(hs, synth, torch, synth.full_schedule())
+        res["full_schedule"] = run_loop(hs, synth, torch, synth.full_schedule(), reps=3,
+                                        breakdown=True)
     if args.pair:
         print("bench: aggressive pair loop", file=sys.stderr, flush=True)
         res["aggressive_pair"] = run_loop(hs, synth, torch, synth.aggressive_pair())
