@@ -64,6 +64,13 @@ def test_attention_random(hs, case):
     hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
     torch.cuda.synchronize()
     attn_close(host_bits(o), want, f"random {ATTN[case]}")
+    # the workspace entry point (the sampler's): with few query tiles, most of these shapes
+    # split their key ranges
+    ow = torch.empty_like(o)
+    hs.hsa_attention_active_ws(bits_dev(q), bits_dev(k), bits_dev(v), ow, scale,
+                               hs.attention_workspace(A, N, B, H, D))
+    torch.cuda.synchronize()
+    attn_close(host_bits(ow), want, f"random {ATTN[case]} with workspace")
 
 
 @pytest.mark.parametrize("case", range(len(SCHED)))
