@@ -223,3 +223,30 @@ def test_attention_plan(hs):
         full, tail, s, keys = plan(a, n, 2, 40)
         if s > 1:
             assert n - (s - 1) * keys >= 256                       # every range >= 8 blocks
+
+
+def test_attention_plan_invariants(hs):
+    """The planner on 3000 seeded random shapes, device sizes and workspaces: whole rounds stay
+    whole, only a partly filled last round is split, every key range is at least 8 key blocks
+    and a multiple of 32 keys, the ranges cover all keys, the pieces fit the workspace and the
+    512-piece limit, and a split never lengthens the launch (in whole-tile units)."""
+    r = np.random.default_rng(77)
+    piece = hs.hsastep_attention_workspace_bytes(256 * 64, 4096, 1, 1, 128) // 512  # 64 tiles x 8 > 512
+    for _ in range(3000):
+        a = int(r.integers(1, 200001)) if r.random() < 0.5 else int(r.integers(1, 3000))
+        n = int(r.integers(256, 200001))
+        b, h = int(r.integers(1, 4)), int(r.integers(1, 65))
+        cus = int(r.choice([8, 64, 80, 120, 256, 304]))
+        full_ws = hs.hsastep_attention_workspace_bytes(a, n, b, h, 128)
+        w = int(r.choice([0, full_ws, int(full_ws * r.random())]))
+        full, tail, s, keys = hs.hsastep_attention_plan(a, n, b, h, 128, cus, w)
+        tiles = -(-a // 256) * h * b
+        if s == 1:
+            assert (full, tail, keys) == (tiles, 0, 0), (a, n, b, h, cus, w)
+            continue
+        assert w > 0 and 2 <= s <= 8
+        assert full + tail == tiles and full % cus == 0 and 0 < tail < cus
+        assert tail * s <= 512 and tail * s * piece <= w
+        assert keys % 32 == 0 and keys >= 256
+        assert (s - 1) * keys < n <= s * keys and n - (s - 1) * keys >= 256
+        assert full // cus + -(-tail * s // cus) / s <= -(-tiles // cus)
