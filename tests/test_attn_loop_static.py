@@ -191,3 +191,88 @@ def test_checker_catches_a_sum_of_unrounded_exponentials():
             test_block_sum_is_the_sum_of_the_rounded_p()
     finally:
         GEN.softmax_part = orig
+
+
+def _run_two_lanes(ops, regs, sgpr):
+    """Executes the fast loop's reference-max set-up on the two lanes of one query (lane 1 is
+    lane 0's partner, lane ^ 32): max3/max/mul/mov/xor per lane, ds_bpermute from the partner."""
+    f = lambda reg, r: np.uint32(reg[r]).view(np.float32)
+    put = lambda reg, r, x: reg.__setitem__(r, int(np.float32(x).view(np.uint32)))
+    def val(reg, t):
+        if t.startswith("v"):
+            return f(reg, int(t[1:]))
+        if t.startswith("s"):
+            return np.uint32(sgpr[int(t[1:])]).view(np.float32)
+        raise AssertionError(t)
+    for op in ops:
+        if op.startswith("s_waitcnt"):
+            continue
+        name, rest = op.split(None, 1)
+        a = [t.strip() for t in rest.split(",")]
+        d = int(a[0][1:])
+        if name == "ds_bpermute_b32":
+            src = int(a[2][1:])
+            got = [regs[1][src], regs[0][src]]
+            for lane in (0, 1):
+                regs[lane][d] = got[lane]
+            continue
+        for reg in regs:
+            if name == "v_max3_f32":
+                put(reg, d, max(val(reg, a[1]), val(reg, a[2]), val(reg, a[3])))
+            elif name == "v_max_f32":
+                put(reg, d, max(val(reg, a[1]), val(reg, a[2])))
+            elif name == "v_mul_f32":
+                put(reg, d, np.float32(val(reg, a[1]) * val(reg, a[2])))
+            elif name == "v_mov_b32":
+                reg[d] = reg[int(a[1][1:])]
+            elif name == "v_xor_b32":
+                reg[d] = int(a[1], 16) ^ reg[int(a[2][1:])]
+            else:
+                raise AssertionError(op)
+
+
+def test_fast_loop_reference_max_is_the_first_blocks_max():
+    """The fast loop's prologue sets the reference max of a query block to c times the max of
+    the first key block's 32 scores over both lanes of the query (and -m beside it), so the
+    following softmax gives p = 1 exactly for the max key and no p above 1."""
+    rng = np.random.default_rng(9)
+    sc = np.float32(0.1275)
+    for par, qb in ((0, 0), (0, 1)):
+        for trial in range(20):
+            scores = (rng.standard_normal((2, 16)) * 30).astype(np.float32)
+            regs = [dict(), dict()]
+            for lane in (0, 1):
+                for j in range(16):
+                    regs[lane][GEN.S(par, qb) + j] = int(scores[lane, j].view(np.uint32))
+            sgpr = {GEN.SC: int(sc.view(np.uint32)), GEN.NINF: int(np.float32(-np.inf).view(np.uint32))}
+            _run_two_lanes(GEN.init_reference_max(par, qb), regs, sgpr)
+            want = np.float32(sc * scores.max())
+            for lane in (0, 1):
+                assert np.uint32(regs[lane][GEN.M + qb]) == want.view(np.uint32)
+                assert np.uint32(regs[lane][GEN.NEGM + qb]) == (-want).view(np.uint32)
+                _run_valu(GEN.softmax_full(par, qb), regs[lane], {GEN.SC: int(sc.view(np.uint32))})
+                p = [np.uint32(((regs[lane][GEN.P(par, qb) + t] >> (16 * h)) & 0xFFFF) << 16).view(np.float32)
+                     for t in range(8) for h in (0, 1)]
+                assert max(p) <= 1.0
+                if scores[lane].max() == scores.max():
+                    assert max(p) == 1.0
+
+
+def test_checker_catches_a_reference_max_of_one_lane():
+    """Planted mistake: without the exchange with the partner lane each lane takes only its own
+    16 scores' max, which the check above catches."""
+    orig = GEN.init_reference_max
+    def own_max(par, qb):
+        out = []
+        for l in orig(par, qb):
+            if l.startswith("ds_bpermute_b32"):
+                dst, _, src = [t.strip() for t in l.split(None, 1)[1].split(",")]
+                l = f"v_mov_b32 {dst}, {src}"      # the lane's own max instead of its partner's
+            out.append(l)
+        return out
+    GEN.init_reference_max = own_max
+    try:
+        with pytest.raises(AssertionError):
+            test_fast_loop_reference_max_is_the_first_blocks_max()
+    finally:
+        GEN.init_reference_max = orig
