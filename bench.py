@@ -2,7 +2,7 @@
 """Benchmark of one HSA denoise iteration on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-loop]
-                    [--no-streaming] [--pair] [--sweep] [--split] [--proj]
+                    [--no-streaming] [--no-mfma-ceiling] [--pair] [--sweep] [--split] [--proj]
 
 A step is one pass of the whole path over the single-step workload (N = 32760
 tokens on a 21x30x52 latent grid, 12 heads x 128, 64 latent channels, half of
@@ -13,7 +13,9 @@ seeded synthetic data already resident in HBM.  Prints one JSON line.
 
 value = attention FLOPs of the iteration (4 * |A| * N * H * D) / wall time of the
 whole iteration, in TFLOP/s; ms_per_step is that wall time.  The roofline entry
-is the attention kernel alone, timed with HIP events around each launch.
+is the attention kernel alone, timed with HIP events around each launch; mfma_ceiling
+is the sustained rate of the same MFMA instruction with nothing else in the loop, and
+attention's fraction of it.
 The full 40-iteration, 30-layer schedule (T=40, budgets {40,20,10,5}, m=4) is also run
 once and its mean ms per iteration reported (the metric's second half), as are the
 HBM-bound kernels one by one with their fraction of 8 TB/s and a plain-copy ceiling at the
@@ -56,6 +58,8 @@ def parse():
                    help="skip the full 40-iteration, 30-layer schedule (run by default)")
     p.add_argument("--no-streaming", action="store_true",
                    help="skip the per-kernel HBM figures and the copy ceiling (run by default)")
+    p.add_argument("--no-mfma-ceiling", action="store_true",
+                   help="skip the sustained MFMA rate probe (run by default, ~0.5 s)")
     p.add_argument("--pair", action="store_true",
                    help="also run the aggressive cond/uncond pair: B=2, N=75600, 40x128 heads, "
                         "40 layers, T=40 {40,10,5} over 10/30/60%%, m=2 (~2-3 minutes, 124 GB "
@@ -193,6 +197,40 @@ def _event_ms(torch, fn, reps, flush=None):
         b.record()
     torch.cuda.synchronize()
     return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def run_mfma_ceiling(hs, synth, torch, attn_tflops, rounds=2000, reps=12):
+    """The sustained rate of the attention kernel's MFMA (32x32x16 bf16) with nothing else in
+    the loop, from the library's probe: 1024 workgroups of 4 wavefronts, 64 * rounds
+    independent MFMAs per wavefront, about 20 ms per launch.  The first launches run while the
+    chip's clock settles under the load, so the figure is the median of the last 8.  Finite
+    operands (seeded, |x| in [0.25, 2)) give the ceiling an MFMA-bound kernel can reach; zero
+    operands draw less power and give the optimistic one."""
+    r = np.random.default_rng(7)
+    vals = (r.uniform(0.25, 2.0, hs.MFMA_PROBE_OPERANDS)
+            * r.choice([-1.0, 1.0], hs.MFMA_PROBE_OPERANDS)).astype(np.float32)
+    finite = torch.from_numpy(synth.f32_to_bf16_bits(vals).view(np.int16)).cuda()
+    zeros = torch.zeros_like(finite)
+    workgroups = 1024
+    sink = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    out = {"instruction": "v_mfma_f32_32x32x16_bf16", "workgroups": workgroups,
+           "mfmas_per_wave": 64 * rounds}
+    for tag, ops in (("finite_operands", finite), ("zero_operands", zeros)):
+        flops = 0.0
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record()
+            flops = hs.hsastep_mfma_probe(ops, sink, rounds, workgroups)
+            b.record()
+        torch.cuda.synchronize()
+        rates = [flops / (a.elapsed_time(b) * 1e-3) / 1e12 for a, b in evs]
+        out[tag + "_tflops"] = float(np.median(rates[-8:]))
+        if tag == "finite_operands" and not np.isfinite(sink.cpu().numpy()).all():
+            raise RuntimeError("mfma probe produced a non-finite sum")
+    out["attention_frac_of_finite_ceiling"] = attn_tflops / out["finite_operands_tflops"]
+    return out
 
 
 def run_streaming(hs, synth, torch, st, reps=20):
@@ -702,6 +740,9 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic},
     }
+    if not args.no_mfma_ceiling:
+        print("bench: sustained MFMA ceiling", file=sys.stderr, flush=True)
+        res["mfma_ceiling"] = run_mfma_ceiling(hs, synth, torch, achieved)
     if not args.no_streaming:
         print("bench: streaming kernels and copy ceiling", file=sys.stderr, flush=True)
         res["streaming_kernels"] = run_streaming(hs, synth, torch, st)

@@ -11,6 +11,8 @@
  *   hsa_euler_step        cached Euler update of all N latents
  * and, fusing the model's projection with the cache write:
  *   hsa_qkv_project       Q/K/V of the active rows; K/V straight into their cache slots
+ * and one measurement utility:
+ *   hsastep_mfma_probe    the sustained bf16 MFMA rate the attention kernel runs against
  *
  * Pages that define the operations (cited below by short name):
  *   [HSA-nl] "Technische Samenvatting: Heterogene Staptoewijzing (HSA) voor
@@ -282,6 +284,26 @@ int hsa_qkv_project(const uint16_t* x_active, const uint16_t* w_qkv, const uint1
 int hsa_euler_step(float* x, float* v_cache, const float* v_fresh, const int32_t* active_pos,
                    int64_t n_active, int64_t n_tokens, int32_t channels, float sigma_cur,
                    float sigma_next, void* stream);
+
+/*
+ * Measurement utility, not a step of the method: the sustained rate of the bf16
+ * matrix instruction the attention kernel is built on (32x32x16, fp32
+ * accumulate), on every compute unit.  The chip's quoted dense peak assumes its
+ * full clock; under sustained matrix load it holds a lower one, so this rate is
+ * the ceiling an MFMA-bound kernel such as hsa_attention_active can approach.
+ * Each workgroup runs 4 wavefronts; each wavefront issues 64 * rounds
+ * independent MFMAs (32*32*16*2 flops each), i.e. one launch performs
+ * workgroups * 4 * 64 * rounds * 32768 flops.  Time it with events around the
+ * call.  Zero operands draw less power and measure a higher, optimistic rate.
+ *
+ *   operands     [1024 * 8] bf16 bit patterns, read once per wavefront (the
+ *                first 512 groups of 8 are the A operands, the rest B)
+ *   sink         [workgroups * 256] fp32 out: per-lane sums of the
+ *                accumulators, so no instruction can be dropped
+ *   rounds       1 .. 2^24;  workgroups  1 .. 2^20
+ */
+int hsastep_mfma_probe(const uint16_t* operands, float* sink, int32_t rounds,
+                       int32_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }

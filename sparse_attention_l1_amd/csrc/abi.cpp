@@ -345,6 +345,17 @@ HSASTEP_API int hsa_qkv_project(const uint16_t* x_active, const uint16_t* w_qkv,
                     "qkv projection");
 }
 
+HSASTEP_API int hsastep_mfma_probe(const uint16_t* operands, float* sink, int32_t rounds,
+                                   int32_t workgroups, void* stream) {
+  if (!operands || !sink) return fail(HSASTEP_ERR_ARG, "null pointer argument");
+  if (!aligned16(operands)) return fail(HSASTEP_ERR_ARG, "operands must be 16-byte aligned");
+  if (rounds < 1 || rounds > (1 << 24) || workgroups < 1 || workgroups > (1 << 20))
+    return fail(HSASTEP_ERR_ARG, "need 1 <= rounds <= 2^24 and 1 <= workgroups <= 2^20");
+  return hip_status(hsastep::launch_mfma_probe(operands, sink, rounds, workgroups,
+                                               as_stream(stream)),
+                    "mfma probe");
+}
+
 HSASTEP_API int hsa_euler_step(float* x, float* v_cache, const float* v_fresh,
                                const int32_t* active_pos, int64_t n_active, int64_t n_tokens,
                                int32_t channels, float sigma_cur, float sigma_next, void* stream) {

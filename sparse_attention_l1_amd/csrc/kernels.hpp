@@ -73,6 +73,10 @@ hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w, const uint16
                               hipStream_t stream);
 
 // euler.hip: cached Euler update over all tokens.
+// sustained bf16 MFMA rate probe (measurement utility): 64 MFMAs per wavefront per round
+hipError_t launch_mfma_probe(const uint16_t* operands, float* sink, int rounds, int workgroups,
+                             hipStream_t stream);
+
 hipError_t launch_euler(float* x, float* v_cache, const float* v_fresh, const int32_t* active_pos,
                         int64_t n_active, int64_t n_tokens, int channels, float sigma_cur,
                         float sigma_next, hipStream_t stream);

@@ -46,6 +46,7 @@ _SIGS = {
     "hsa_euler_step": ([_p, _p, _p, _p, _i64, _i64, _i32, _f, _f, _p], ctypes.c_int),
     "hsa_qkv_project": ([_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _i32, _p],
                         ctypes.c_int),
+    "hsastep_mfma_probe": ([_p, _p, _i32, _i32, _p], ctypes.c_int),
 }
 for _name, (_args, _ret) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -308,3 +309,17 @@ def hsa_euler_step(x: torch.Tensor, v_cache: torch.Tensor, v_fresh: torch.Tensor
                               _dev(active_pos, "active_pos", (torch.int32,)), n_active, n, c,
                               float(sigma_cur), float(sigma_next), _stream(stream)),
            "hsa_euler_step")
+
+
+MFMA_PROBE_OPERANDS = 1024 * 8     # bf16 values the probe reads
+
+
+def hsastep_mfma_probe(operands: torch.Tensor, sink: torch.Tensor, rounds: int,
+                       workgroups: int, stream=None) -> float:
+    """Launch the sustained-MFMA-rate probe; returns the flops one launch performs."""
+    if operands.numel() != MFMA_PROBE_OPERANDS or sink.numel() < workgroups * 256:
+        raise ValueError("operands must hold 8192 bf16 values and sink workgroups*256 floats")
+    _check(lib.hsastep_mfma_probe(_dev(operands, "operands", _BF16),
+                                  _dev(sink, "sink", (torch.float32,)), rounds, workgroups,
+                                  _stream(stream)), "hsastep_mfma_probe")
+    return float(workgroups) * 4 * 64 * rounds * 32 * 32 * 16 * 2
