@@ -303,17 +303,25 @@ def check_proj_hazards(gen):
 
 
 def check_proj_lds_bounds(gen, lds_bytes=LDS_BYTES):
-    """Fragment reads: row R < 256 of a 128-byte-row region, any chunk, plus the immediate
-    offset (the W addresses carry the W region base); tile loads: m0 immediate plus the
-    wavefront's 1 KB slot row."""
+    """Fragment reads: the address register of k-step u holds, per lane, row 128 w + lq of
+    the X (or W) region, chunk (4u + g) ^ swizzle (w = 0, 1; lq < 16; g < 4); the immediate
+    adds the buffer and 2048 bytes per row block.  Each read must stay inside the 32 KB half
+    of the stage buffer its immediate names.  Tile loads: m0 immediate plus the wavefront's
+    1 KB slot row."""
     errors = []
-    row_end = max(r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 16 for r in range(256) for c in range(8))
+    span = max((w * 128 + lq) * 128 + 16 * ((4 * u + g) ^ (((w * 128 + lq) >> 1) & 7)) + 16
+               for w in range(2) for lq in range(16) for u in range(2) for g in range(4))
+    half = gen.XBUF[1] - gen.XBUF[0]
     for line in gen.generate():
         m = re.search(r"offset:(\d+)", line)
         if line.startswith("ds_read_b128") and m:
             addr = int(re.search(r"v(\d+) offset", line).group(1))
-            base = gen.WBUF[0] if gen.WADDR <= addr < gen.WADDR + 16 else 0
-            if base + row_end + int(m.group(1)) > lds_bytes:
+            off = int(m.group(1))
+            is_w = gen.WADDR <= addr < gen.WADDR + 2
+            base = gen.WBUF[0] if is_w else 0
+            lo = base + off
+            region = (gen.WBUF if is_w else gen.XBUF)[off // half]
+            if lo + span > region + half or lo < region or lo + span > lds_bytes:
                 errors.append(line)
         m0 = re.match(r"s_add_u32 m0, s\d+, (\d+)", line)
         if m0 and int(m0.group(1)) + 3 * 1024 + 1024 > lds_bytes:
@@ -321,15 +329,16 @@ def check_proj_lds_bounds(gen, lds_bytes=LDS_BYTES):
     return errors
 
 
-def proj_stage_walk(gen, nstage, max_instructions=200000):
+def proj_stage_walk(gen, nstage, max_instructions=200000, rot=0):
     """Runs the generated loop's control flow for one wavefront with nstage stages, modelling
     the scalar registers it uses (stage counter, descriptor offset and range), the tile loads
     (which stage and which buffer part each fetches), vmcnt waits, barriers and fragment
-    reads.  Returns (stages read per k-step, list of errors)."""
+    reads.  The tile starts at stage rot and wraps (its descriptors begin rot columns in).
+    Returns (stages read per k-step, list of errors)."""
     body = [l for l in gen.generate() if not l.startswith(";")]
     labels = {l[:-1]: i for i, l in enumerate(body) if l.endswith(":")}
-    sreg = {gen.NSTAGE: nstage}
-    desc_off = {gen.XDESC: 0, gen.WDESC: 0}
+    sreg = {gen.NSTAGE: nstage, gen.WRAPT: nstage - rot, gen.WRAPB: nstage * 128}
+    desc_off = {gen.XDESC: rot * 128, gen.WDESC: rot * 128}
     desc_live = {gen.XDESC: True, gen.WDESC: True}
     scc, m0, pc, steps = False, None, 0, 0
     inflight, content, errors, reads = [], {}, [], []
@@ -361,10 +370,19 @@ def proj_stage_walk(gen, nstage, max_instructions=200000):
         elif op in ("s_cmp_ge_u32", "s_cmp_eq_u32"):
             x, y = val(ops[0]), val(ops[1])
             scc = x >= y if op == "s_cmp_ge_u32" else x == y
+        elif op == "s_sub_u32":
+            d = int(ops[0][1:])
+            if d in desc_off:
+                desc_off[d] -= val(ops[2])
+            else:
+                sreg[d] = val(ops[1]) - val(ops[2])
         elif op == "s_cselect_b32":
-            d = int(ops[0][1:]) - 2
-            if scc and d in desc_live:
-                desc_live[d] = False
+            d = int(ops[0][1:])
+            if d - 2 in desc_live:
+                if scc:
+                    desc_live[d - 2] = False
+            else:
+                sreg[d] = val(ops[1]) if scc else val(ops[2])
         elif op == "s_cbranch_scc1":
             if scc:
                 pc = labels[ops[0]]
@@ -377,6 +395,8 @@ def proj_stage_walk(gen, nstage, max_instructions=200000):
             buf = (m0 % gen.WBUF[0]) // (gen.XBUF[1] - gen.XBUF[0])
             part = ("X" if d == gen.XDESC else "W", (m0 % (gen.XBUF[1] - gen.XBUF[0])) // gen.LOAD_BYTES)
             st = desc_off[d] // 128 if desc_live[d] else None
+            if st is not None and not 0 <= desc_off[d] < nstage * 128:
+                errors.append(f"load at column offset {desc_off[d]} outside the rows")
             if buf in last_read and not any(last_read[buf] < b for b in barriers):
                 errors.append(f"load into buffer {buf} with no barrier after its last read")
             inflight.append((buf, part, st))
@@ -402,7 +422,8 @@ def proj_stage_walk(gen, nstage, max_instructions=200000):
             reads.append(got.pop() if len(got) == 1 else "?")
     if sreg.get(gen.STAGE) != nstage:
         errors.append(f"loop ended after {sreg.get(gen.STAGE)} stages, not {nstage}")
-    for st in range(nstage):
-        if sorted(stage_loads.get(st, [])) != sorted((st % 2, (t, i)) for t in "XW" for i in range(8)):
+    for t in range(nstage):
+        st = (rot + t) % nstage
+        if sorted(stage_loads.get(st, [])) != sorted((t % 2, (x, i)) for x in "XW" for i in range(8)):
             errors.append(f"stage {st} loaded as {stage_loads.get(st)}")
-    return [reads[i] for i in range(0, len(reads), 8)], errors
+    return [reads[i] for i in range(0, len(reads), gen.READS)], errors

@@ -28,21 +28,24 @@ def test_lds_offsets_in_bounds():
     assert lc.check_proj_lds_bounds(GEN) == []
 
 
-@pytest.mark.parametrize("nstage", [1, 2, 3, 4, 5, 24, 80])
+@pytest.mark.parametrize("nstage", [1, 2, 3, 4, 5, 24, 79, 80])
 def test_stage_walk(nstage):
-    """Every stage loaded once into buffer stage % 2, and read four times (one per k-step),
-    in order; the last group of reads (the next stage's k-step 0, after the end) reads the
+    """For every start stage rot: the t-th stage of the walk, column (rot + t) mod nstage, is
+    loaded once into buffer t % 2, from inside the rows, and read once per k-step (two), in
+    order; the last group of reads (the next stage's k-step 0, after the end) reads the
     empty-range loads and is unused."""
-    ksteps, errors = lc.proj_stage_walk(GEN, nstage)
-    assert errors == []
-    assert ksteps[:-1] == [s for s in range(nstage) for _ in range(4)]
-    assert ksteps[-1] is None
+    rots = range(nstage) if nstage < 30 else (0, 1, nstage // 2, nstage - 2, nstage - 1)
+    for rot in rots:
+        ksteps, errors = lc.proj_stage_walk(GEN, nstage, rot=rot)
+        assert errors == [], (rot, errors[:3])
+        assert ksteps[:-1] == [(rot + t) % nstage for t in range(nstage) for _ in range(GEN.KSTEPS)]
+        assert ksteps[-1] is None
 
 
 def test_loop_shape():
     body = GEN.generate()
     loop = body[body.index(".Lploop:"):body.index("s_branch .Lploop")]
-    assert sum(l.startswith("v_mfma") for l in loop) == 2 * 64        # two stages of 4 x 16
+    assert sum(l.startswith("v_mfma") for l in loop) == 2 * 128       # two stages of 2 x 64
     assert sum(l == "s_barrier" for l in loop) == 2                   # one per stage
     assert sum(l.startswith("buffer_load") for l in loop) == 2 * 16
     assert sum(l.startswith("ds_read_b128") for l in loop) == 2 * 32
@@ -71,6 +74,15 @@ def test_walk_catches_a_missing_load_wait():
     errs = _patched("stage", lambda f: lambda par: [l.replace("vmcnt(0) ", "") for l in f(par)],
                     _walk_errors)
     assert any("incomplete" in e or "still loads" in e for e in errs)
+
+
+def test_walk_catches_a_missing_wrap():
+    """Without the move back at the wrap point the loads run past the end of the rows."""
+    def nowrap(f):
+        return lambda ahead: [l for l in f(ahead) if not l.startswith("s_sub")]
+    errs = _patched("advance", nowrap,
+                    lambda: [e for n in (3, 5) for e in lc.proj_stage_walk(GEN, n, rot=2)[1]])
+    assert any("outside the rows" in e for e in errs)
 
 
 def test_walk_catches_a_wrong_descriptor_advance():
