@@ -106,6 +106,29 @@ def test_qkv_project_unaligned_many_tiles(hs):
     run_case(hs, 1, 9000, 12000, 8, 96, 1024, True, seed=21, sample=rows, misalign=True)
 
 
+@pytest.mark.parametrize("B,A,N,H,D,Dm,with_bias", [
+    (2, 300, 500, 3, 64, 4096, True),     # 64 stages: the smallest rotated reduction, 9 tiles
+    (1, 700, 1000, 8, 64, 4160, False),   # 65 stages (odd), ragged tiles, 18 rotations
+])
+def test_qkv_project_rotated_start(hs, B, A, N, H, D, Dm, with_bias):
+    """Reductions of 64 stages or more start at a per-tile stage and wrap around."""
+    run_case(hs, B, A, N, H, D, Dm, with_bias, seed=A + Dm)
+
+
+def test_qkv_project_rotated_many_tiles_unaligned(hs):
+    """More tiles than rotation positions (96), on the per-value store path."""
+    rows = synth.sample_rows(1, 2000, 48, tag=7)
+    run_case(hs, 1, 2000, 3000, 16, 64, 4096, True, seed=23, sample=rows, misalign=True)
+
+
+def test_qkv_project_model_dim_5120(hs):
+    """The pair's projection shape at model dim 5120 (80 stages, 3540 tiles over 40 x 128
+    heads, batch 2, bias) on a smaller cache: 64 sampled rows against the oracle, every
+    stale cache row bit for bit."""
+    rows = synth.sample_rows(2, 7560, 32, tag=9)
+    run_case(hs, 2, 7560, 8000, 40, 128, 5120, True, seed=29, sample=rows)
+
+
 def test_qkv_project_full_size_single_step(hs):
     """16380 active rows of a 32760-token cache, 12 x 128 heads, model dim 1536: every stale
     row checked bit for bit, 64 sampled rows against the oracle."""
