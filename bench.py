@@ -688,7 +688,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the HSA path is built and "
-              f"timed on a single MI355X; multi-GPU sharding is not part of this build.",
+              f"timed on a single MI355X; sharding across GPUs is not implemented.",
               file=sys.stderr)
         sys.exit(2)
     import torch
