@@ -161,6 +161,17 @@ def test_kv_attention_euler_gather_reject(hs):
     assert ga(None, None, None, 0, 8, 8, None) == hs.OK
 
 
+def test_mfma_probe_rejects(hs):
+    f = lambda *a: call(hs, "hsastep_mfma_probe", *a)
+    assert f(None, FAKE, 1, 1, None) == hs.ERR_ARG
+    assert f(FAKE, None, 1, 1, None) == hs.ERR_ARG
+    assert f(ctypes.c_void_p((1 << 20) + 2), FAKE, 1, 1, None) == hs.ERR_ARG     # misaligned
+    assert f(FAKE, FAKE, 0, 1, None) == hs.ERR_ARG
+    assert f(FAKE, FAKE, (1 << 24) + 1, 1, None) == hs.ERR_ARG
+    assert f(FAKE, FAKE, 1, 0, None) == hs.ERR_ARG
+    assert f(FAKE, FAKE, 1, (1 << 20) + 1, None) == hs.ERR_ARG
+
+
 def test_qkv_project_rejects(hs):
     f = lambda *a: call(hs, "hsa_qkv_project", *a)
     assert f(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 8, 1, 2, 64, 96, None) == hs.ERR_UNSUPPORTED
