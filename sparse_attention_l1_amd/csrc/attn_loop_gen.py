@@ -43,8 +43,10 @@ more than these 24 extra VALU instructions per block.)
 
 Two bodies: generate(True) is the checked loop described above; generate(False) is the fast
 loop, which sets each query block's reference max from key block 0 in the prologue and then
-drops every range check (the block sums only go into L), so no step has a data-dependent
-branch.  Its labels carry an F after .L so that both bodies can sit in one kernel; the kernel
+drops every range check (the block sums only go into L) and the ragged-block masks, so no
+step has a data-dependent branch or a test.  Its keys past the end of the last block keep
+s = 0 (their K and V rows read as zero), so each adds exactly bf16(2^-m) to the row sum and
+nothing to O; the kernel subtracts that from L afterwards.  Its labels carry an F after .L so that both bodies can sit in one kernel; the kernel
 runs the checked body only for workgroups with a query whose fast row sum left [1, 2^64].
 
 Register map (per lane):  VGPR  S 0-63, P 64-95, K fragments 96-159, LDS/buffer addresses
@@ -376,8 +378,12 @@ def step(r, checked=True):
         out.extend(add_block_sums((q, 0), (p, 1)))
     # ---------------- H2: PV(s,1) [VF[p], P[p][1]] and PV(s+1,0) [VF[q], P[q][0]]
     kr = [kread(x3, u) for u in range(8)]
-    valu = (mask_call(q, 1, MASK1, f".Lm{r}a") + mask_call(p, 0, MASK0, f".Lm{r}b") +
-            merge(softmax_part(q, 1, 0, 4), softmax_part(p, 0, 0, 4)))
+    # the ragged last block: the checked body masks its keys past the end (s = -inf); the fast
+    # body leaves them at s = 0 (their K rows read as zero, their V rows too) and the kernel
+    # takes their p out of the row sum afterwards
+    masks = (mask_call(q, 1, MASK1, f".Lm{r}a") + mask_call(p, 0, MASK0, f".Lm{r}b")
+             if checked else [])
+    valu = masks + merge(softmax_part(q, 1, 0, 4), softmax_part(p, 0, 0, 4))
     # slots 1-14: the half's last MFMA slot, which the loop control and the next step's LDS
     # wait follow, carries no softmax work (0.7% faster than slots 1-15, measured on MI355X)
     plan = place(valu, list(range(1, 15)))

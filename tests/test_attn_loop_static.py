@@ -31,9 +31,11 @@ def test_lds_offsets_in_bounds(checked):
 
 
 def test_fast_body_shape():
-    """The fast body: the same loop without any range check or data-dependent branch, its
-    labels distinct from the checked body's, and each query block's reference max set from
-    key block 0 before that block's first exponential."""
+    """The fast body: the same loop without any range check, ragged-block test or
+    data-dependent branch (the same MFMAs, LDS reads, tile loads and barriers in the same
+    order, and as many exponentials), its labels distinct from the checked body's, and each
+    query block's reference max set from key block 0 before that block's first
+    exponential."""
     fast, checked = GEN.generate(False), GEN.generate(True)
     assert not any(l.startswith(("s_cbranch_vccnz", "v_cmp_nge_f32")) for l in fast)
     assert any(l.startswith("s_cbranch_vccnz") for l in checked)
@@ -41,8 +43,12 @@ def test_fast_body_shape():
     assert labels(fast) and not labels(fast) & labels(checked)
     loop_f = fast[fast.index(".LFloop:"):fast.index("s_branch .LFloop")]
     loop_c = checked[checked.index(".Lloop:"):checked.index("s_branch .Lloop")]
-    strip = lambda body: [l for l in body if l.startswith(("v_mfma", "ds_read", "buffer_load", "s_barrier", "v_exp"))]
+    strip = lambda body: [l for l in body if l.startswith(("v_mfma", "ds_read", "buffer_load", "s_barrier"))]
     assert strip(loop_f) == strip(loop_c)
+    n_exp = lambda body: sum(l.startswith("v_exp") for l in body)
+    assert n_exp(loop_f) == n_exp(loop_c)
+    assert not any(l.startswith("s_cbranch_scc1") and "_call" in l for l in loop_f)
+    assert any(l.startswith("s_cbranch_scc1") and "_call" in l for l in loop_c)
     first_exp = next(i for i, l in enumerate(fast) if l.startswith("v_exp_f32"))
     for qb in (0, 1):
         sets_m = [i for i, l in enumerate(fast) if l.startswith(f"v_mov_b32 v{GEN.M + qb},")]

@@ -234,6 +234,39 @@ def test_attention_fallback_per_query(hs, N):
     attn_close(host_bits(o3), want, f"fallback per query, split, N{N}")
 
 
+@pytest.mark.parametrize("N", [1000, 1009, 4097])
+def test_attention_ragged_last_block(hs, N):
+    """The fast loop does not mask the keys past the end of a ragged last block; it takes their
+    p back out of the row sum.  Every second query here has a negative first-block max (its
+    keys 0..31 point away from it), so a padded key's p would exceed 1: those queries go to the
+    checked loop, which masks, and the rest keep the fast loop's corrected sum.  Against the
+    oracle, also through the split path, and a query's bits do not depend on its neighbours."""
+    B, A, H, D = 1, 300, 2, 128
+    r = np.random.default_rng(N + 11)
+    qf = r.standard_normal((B, A, H, D)).astype(np.float32)
+    kf = r.standard_normal((B, N, H, D)).astype(np.float32)
+    qf[:, ::2, :, 0] = -8.0
+    kf[:, :32, :, 0] = 8.0
+    q, k = synth.f32_to_bf16_bits(qf), synth.f32_to_bf16_bits(kf)
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, N, H, D)).astype(np.float32))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    want = oracle.attention_active(q, k, v, scale)
+    o = torch.empty((B, A, H, D), dtype=torch.int16, device="cuda")
+    hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
+    torch.cuda.synchronize()
+    attn_close(host_bits(o), want, f"ragged last block N{N}")
+    sub = np.arange(1, A, 2)
+    o2 = torch.empty((B, sub.size, H, D), dtype=torch.int16, device="cuda")
+    hs.hsa_attention_active(bits_dev(q[:, sub]), bits_dev(k), bits_dev(v), o2, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(o2), host_bits(o)[:, sub])
+    ws = hs.attention_workspace(A, N, B, H, D)
+    o3 = torch.empty_like(o)
+    hs.hsa_attention_active_ws(bits_dev(q), bits_dev(k), bits_dev(v), o3, scale, ws)
+    torch.cuda.synchronize()
+    attn_close(host_bits(o3), want, f"ragged last block, split, N{N}")
+
+
 @pytest.mark.parametrize("D,N,key", [(128, 1000, 3), (128, 1000, 700), (64, 500, 300)])
 def test_attention_nan_key(hs, D, N, key):
     """A NaN in one cached key of head 1 makes every score of that head NaN, so the oracle's
