@@ -267,6 +267,26 @@ def test_attention_ragged_last_block(hs, N):
     attn_close(host_bits(o3), want, f"ragged last block, split, N{N}")
 
 
+def test_attention_every_last_block_width(hs):
+    """Every width of the last key block, 1 to 32 keys (N = 257 .. 288), with half of the
+    queries on the fast loop's corrected row sum and half (negative first-block max) on the
+    checked loop, against the oracle."""
+    B, A, H, D = 1, 96, 2, 128
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    for N in range(257, 289):
+        r = np.random.default_rng(N)
+        qf = r.standard_normal((B, A, H, D)).astype(np.float32)
+        kf = r.standard_normal((B, N, H, D)).astype(np.float32)
+        qf[:, 1::2, :, 0] = -8.0
+        kf[:, :32, :, 0] = 8.0
+        q, k = synth.f32_to_bf16_bits(qf), synth.f32_to_bf16_bits(kf)
+        v = synth.f32_to_bf16_bits(r.standard_normal((B, N, H, D)).astype(np.float32))
+        o = torch.empty((B, A, H, D), dtype=torch.int16, device="cuda")
+        hs.hsa_attention_active(bits_dev(q), bits_dev(k), bits_dev(v), o, scale)
+        torch.cuda.synchronize()
+        attn_close(host_bits(o), oracle.attention_active(q, k, v, scale), f"last block of {N - 256} keys")
+
+
 @pytest.mark.parametrize("D,N,key", [(128, 1000, 3), (128, 1000, 700), (64, 500, 300)])
 def test_attention_nan_key(hs, D, N, key):
     """A NaN in one cached key of head 1 makes every score of that head NaN, so the oracle's
